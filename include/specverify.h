@@ -1,0 +1,137 @@
+/*
+ * specverify.h -- C ABI of the speculative-decoding verification sampler
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (velog "6-1편. Speculative Decoding", section 2 "알고리즘
+ * 4단계", steps 2-4, and sections 2-1 and 2-2): for every sequence b of a
+ * batch, given the target logits of gamma_b + 1 positions, the draft logits
+ * of gamma_b positions, the gamma_b drafted tokens x_i and gamma_b + 1
+ * uniforms u_i, compute p_i = softmax(target_i / T_b) and
+ * q_i = softmax(draft_i / T_b), accept x_i while u_i < min(1, p_i(x_i) /
+ * q_i(x_i)), and at the first rejection n emit one token sampled (inverse
+ * CDF, token order, uniform u_gamma) from norm(max(0, p_n - q_n)); if all
+ * gamma_b drafts are accepted emit a bonus token sampled from p_gamma.
+ * With T_b = 0 the rule is greedy: accept while x_i equals argmax of the
+ * target logits, emit that argmax at the first mismatch, or the argmax of
+ * the last position as the bonus ("How to Scale Your Model -- All About
+ * Transformer Inference", Appendix D "Speculative Sampling").  The
+ * accepted length stays on the device, so the caller needs no
+ * device-to-host synchronisation to consume it (Perplexity "Accelerating
+ * Sonar through speculation", section "단일 토큰에 대한 MTP 스케줄링": the
+ * sync on the accepted length is what extra GPU work avoids).
+ *
+ * Packed ragged layout.  Sequence b owns draft rows cu_draft[b] ..
+ * cu_draft[b+1] - 1 and target rows cu_t[b] .. cu_t[b] + gamma_b with
+ * cu_t[b] = cu_draft[b] + b (so R_t = R_d + B target rows in total).
+ * A uniform draft length is the special case cu_draft[b] = b * gamma.
+ *
+ * Ownership.  The caller owns every input and output buffer (device
+ * memory).  A handle owns only its device workspace, allocated in
+ * specverify_create and freed in specverify_destroy.  specverify_run
+ * allocates nothing, never synchronises and is asynchronous on the given
+ * stream; consumers of the outputs must be ordered after it on that
+ * stream.  One handle must not have two runs in flight on different
+ * streams at once (they share the workspace); destroy only after the
+ * caller has synchronised with its last run.
+ *
+ * Errors.  Problems visible on the host (NULL pointers, sizes beyond the
+ * handle's limits, logits not aligned to their element size) return a
+ * status before any launch.
+ * Problems in the data are detected on the device per sequence and
+ * reported in accepted_len: -1 = invalid data (a NaN or +inf logit in any
+ * of the sequence's rows, a row of only -inf, a drafted token outside
+ * [0, V), a temperature that is negative, not finite or in (0, FLT_MIN)),
+ * -2 = a bounded wait inside the kernel expired (never in normal
+ * operation; the kernel always terminates).  The tokens of such a
+ * sequence are -1 and its diagnostics unspecified.
+ */
+#ifndef SPECVERIFY_H_
+#define SPECVERIFY_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct specverify_ctx* specverify_handle;
+
+typedef enum {
+  SPECVERIFY_OK = 0,
+  SPECVERIFY_ERR_INVALID_ARGUMENT = 1, /* bad pointer / size / config     */
+  SPECVERIFY_ERR_UNSUPPORTED = 2,      /* unaligned logits, V too big     */
+  SPECVERIFY_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed     */
+  SPECVERIFY_ERR_DEVICE = 4            /* HIP runtime / launch failure    */
+} specverify_status;
+
+typedef enum { SPECVERIFY_F32 = 0, SPECVERIFY_BF16 = 1 } specverify_dtype;
+
+/* Fixed per handle.  Limits: 1 <= vocab <= 524288 (64 chunks of 8192),
+ * max_batch >= 1, max_gamma >= 0, max_batch * (max_gamma + 1) <= 2^24. */
+typedef struct {
+  int32_t max_batch;   /* largest B a run may use                                 */
+  int32_t max_gamma;   /* largest draft length; bounds R_t <= max_batch*(max_gamma+1) */
+  int32_t vocab;       /* V of every logits row                                   */
+  int32_t dtype;       /* specverify_dtype of both logits tensors                 */
+  int32_t device;      /* HIP device ordinal the workspace lives on               */
+  int32_t spin_limit;  /* polls before a wait gives up (0 = default, ~seconds)    */
+} specverify_config;
+
+/* Inputs of one run; every pointer is device memory. */
+typedef struct {
+  int32_t batch;              /* B >= 0 (0 = nothing to do)                        */
+  int32_t gamma;              /* uniform draft length, used iff cu_draft == NULL   */
+  const int32_t* cu_draft;    /* [B+1] prefix offsets of draft rows, or NULL       */
+  int32_t num_draft_rows;     /* R_d = cu_draft[B] (host copy), used iff cu_draft  */
+  const void* target_logits;  /* [R_t, target_stride] f32 or bf16; rows that start on
+                                 16-byte boundaries take the vector-load path       */
+  int64_t target_stride;      /* elements between rows, >= V                       */
+  const void* draft_logits;   /* [R_d, draft_stride]; may be NULL iff R_d == 0     */
+  int64_t draft_stride;
+  const int32_t* draft_tokens;/* [R_d] drafted ids x_i; may be NULL iff R_d == 0   */
+  const float* uniforms;      /* [R_t] u in [0,1): uniforms[cu_t[b]+i], i < gamma_b,
+                                 test draft i; uniforms[cu_t[b]+gamma_b] is the one
+                                 uniform of the final (residual or bonus) sample   */
+  const float* temperatures;  /* [B] T_b; 0 = greedy                               */
+} specverify_inputs;
+
+/* Outputs of one run; device memory owned by the caller. */
+typedef struct {
+  int32_t* accepted_len;      /* [B] n_b in [0, gamma_b]; -1 invalid data; -2 wait expired */
+  int32_t* out_tokens;        /* [R_t] at cu_t[b]+j: x_j for j < n_b, the sampled token at
+                                 j = n_b, -1 for j > n_b (all -1 if n_b < 0)          */
+  float* p_draft;             /* [R_d] p_i(x_i), or NULL                            */
+  float* q_draft;             /* [R_d] q_i(x_i), or NULL                            */
+  float* beta;                /* [R_d] sum_k min(p_i, q_i), or NULL                 */
+  float* resid_mass;          /* [R_d] sum_k max(0, p_i - q_i), or NULL             */
+} specverify_outputs;
+
+/* Allocate a handle and its workspace on cfg->device.  On failure *out is
+ * NULL.  Errors: INVALID_ARGUMENT (NULL or out-of-range config),
+ * UNSUPPORTED (vocab too large), DEVICE (no such device / runtime error),
+ * OUT_OF_MEMORY. */
+specverify_status specverify_create(const specverify_config* cfg, specverify_handle* out);
+
+/* Verify one batch, asynchronously on hip_stream (a hipStream_t; NULL = the
+ * default stream).  Writes accepted_len, out_tokens and the non-NULL
+ * diagnostics; nothing else.  Errors (no launch happens): INVALID_ARGUMENT
+ * for a NULL handle / inputs / outputs or required pointer, B > max_batch,
+ * gamma outside [0, max_gamma], R_t > max_batch * (max_gamma + 1), a
+ * stride < V; UNSUPPORTED for logits pointers not aligned to the element
+ * size; DEVICE if the launch fails. */
+specverify_status specverify_run(specverify_handle h, const specverify_inputs* in,
+                                 const specverify_outputs* out, void* hip_stream);
+
+/* Free the workspace and the handle (NULL is accepted). */
+specverify_status specverify_destroy(specverify_handle h);
+
+/* Number of V-chunks (8192 logits each) a row is split into for this
+ * handle, and the workspace size in bytes; for tools and tests. */
+int32_t specverify_chunks_per_row(specverify_handle h);
+int64_t specverify_workspace_bytes(specverify_handle h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H_ */

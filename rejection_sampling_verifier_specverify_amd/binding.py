@@ -1,0 +1,179 @@
+"""ctypes binding of the C ABI in include/specverify.h.
+
+Argument marshalling only: every step of the verification runs in the HIP
+kernels of libspecverify.so.  The functions keep the C names
+(``specverify_create``, ``specverify_run``, ``specverify_destroy``);
+``SpecVerify`` wraps them for torch tensors, which serve as device memory,
+and the current torch stream.  If the library is missing the import of this
+module succeeds but every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libspecverify.so")
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_OUT_OF_MEMORY, ERR_DEVICE = range(5)
+F32, BF16 = 0, 1
+STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "DEVICE"}
+CHUNK = 8192          # logits per V-chunk (one workgroup)
+EXPORTED = ("specverify_create", "specverify_run", "specverify_destroy",
+            "specverify_chunks_per_row", "specverify_workspace_bytes")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("max_batch", ctypes.c_int32), ("max_gamma", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("device", ctypes.c_int32), ("spin_limit", ctypes.c_int32)]
+
+
+class Inputs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("gamma", ctypes.c_int32),
+                ("cu_draft", ctypes.c_void_p), ("num_draft_rows", ctypes.c_int32),
+                ("target_logits", ctypes.c_void_p), ("target_stride", ctypes.c_int64),
+                ("draft_logits", ctypes.c_void_p), ("draft_stride", ctypes.c_int64),
+                ("draft_tokens", ctypes.c_void_p), ("uniforms", ctypes.c_void_p),
+                ("temperatures", ctypes.c_void_p)]
+
+
+class Outputs(ctypes.Structure):
+    _fields_ = [("accepted_len", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
+                ("p_draft", ctypes.c_void_p), ("q_draft", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("resid_mass", ctypes.c_void_p)]
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, where: str, status: int):
+        super().__init__(f"{where} failed: SPECVERIFY_ERR_{STATUS_NAMES.get(status, status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libspecverify.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(the verifier has no fallback path)")
+    # torch ships its own HIP runtime with the same soname (libamdhip64.so.7).
+    # Importing torch first makes the library bind to that runtime, so that the
+    # process holds one HIP runtime whose device pointers and streams both sides
+    # share; without torch the library binds to the system ROCm runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(path)
+    lib.specverify_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_void_p)]
+    lib.specverify_create.restype = ctypes.c_int
+    lib.specverify_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(Inputs), ctypes.POINTER(Outputs),
+                                   ctypes.c_void_p]
+    lib.specverify_run.restype = ctypes.c_int
+    lib.specverify_destroy.argtypes = [ctypes.c_void_p]
+    lib.specverify_destroy.restype = ctypes.c_int
+    lib.specverify_chunks_per_row.argtypes = [ctypes.c_void_p]
+    lib.specverify_chunks_per_row.restype = ctypes.c_int32
+    lib.specverify_workspace_bytes.argtypes = [ctypes.c_void_p]
+    lib.specverify_workspace_bytes.restype = ctypes.c_int64
+    _lib = lib
+    return lib
+
+
+def specverify_create(cfg: Config) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    st = load_library().specverify_create(ctypes.byref(cfg), ctypes.byref(h))
+    if st != OK:
+        raise SpecVerifyError("specverify_create", st)
+    return h
+
+
+def specverify_run(h: ctypes.c_void_p, inputs: Inputs, outputs: Outputs, stream: int) -> None:
+    st = load_library().specverify_run(h, ctypes.byref(inputs), ctypes.byref(outputs),
+                                       ctypes.c_void_p(stream))
+    if st != OK:
+        raise SpecVerifyError("specverify_run", st)
+
+
+def specverify_destroy(h: ctypes.c_void_p) -> None:
+    st = load_library().specverify_destroy(h)
+    if st != OK:
+        raise SpecVerifyError("specverify_destroy", st)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+class SpecVerify:
+    """A handle bound to one device, vocabulary and logits dtype.
+
+    ``run`` takes torch tensors that already live on the device (target
+    [R_t, V], draft [R_d, V], float32 or bfloat16) and launches on the
+    current torch stream; it returns without synchronising.
+    """
+
+    def __init__(self, max_batch: int, max_gamma: int, vocab: int, dtype: str = "bf16",
+                 device: int = 0, spin_limit: int = 0):
+        self.dtype = {"f32": F32, "bf16": BF16}[dtype]
+        self.vocab = vocab
+        self.device = device
+        self.cfg = Config(max_batch, max_gamma, vocab, self.dtype, device, spin_limit)
+        self.handle = specverify_create(self.cfg)
+        lib = load_library()
+        self.chunks = int(lib.specverify_chunks_per_row(self.handle))
+        self.workspace_bytes = int(lib.specverify_workspace_bytes(self.handle))
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            specverify_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def run(self, target, draft, draft_tokens, uniforms, temperatures, accepted_len, out_tokens, *,
+            gamma: Optional[int] = None, cu_draft=None, num_draft_rows: Optional[int] = None,
+            p_draft=None, q_draft=None, beta=None, resid_mass=None, stream=None) -> None:
+        import torch
+        want = torch.float32 if self.dtype == F32 else torch.bfloat16
+        for name, t in (("target", target), ("draft", draft)):
+            if t is None or t.numel() == 0:
+                continue
+            if t.dtype != want:
+                raise TypeError(f"{name} logits must be {want}, got {t.dtype}")
+            if t.dim() != 2 or t.stride(1) != 1:
+                raise ValueError(f"{name} logits must be a 2-D tensor with unit column stride")
+        batch = int(temperatures.shape[0])
+        inp = Inputs()
+        inp.batch = batch
+        if cu_draft is None:
+            inp.gamma = int(gamma)
+            inp.cu_draft = None
+            inp.num_draft_rows = batch * int(gamma)
+        else:
+            inp.gamma = 0
+            inp.cu_draft = _ptr(cu_draft)
+            inp.num_draft_rows = int(num_draft_rows if num_draft_rows is not None
+                                     else (draft.shape[0] if draft is not None else 0))
+        inp.target_logits = _ptr(target)
+        inp.target_stride = int(target.stride(0))
+        has_draft = draft is not None and draft.numel() > 0
+        inp.draft_logits = _ptr(draft) if has_draft else None
+        inp.draft_stride = int(draft.stride(0)) if has_draft else int(self.vocab)
+        inp.draft_tokens = _ptr(draft_tokens) if has_draft else None
+        inp.uniforms = _ptr(uniforms)
+        inp.temperatures = _ptr(temperatures)
+        out = Outputs(_ptr(accepted_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),
+                      _ptr(beta), _ptr(resid_mass))
+        s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
+        specverify_run(self.handle, inp, out, int(s))

@@ -1,0 +1,54 @@
+"""Host-only checks of the C ABI library: it builds, loads and exports every
+function that include/specverify.h declares; host-side argument checks that
+return before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rejection_sampling_verifier_specverify_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "specverify.h")).read()
+    return sorted(set(re.findall(r"\b(specverify_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = binding.load_library()
+    declared = _declared()
+    assert set(declared) >= set(binding.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layouts_match_header():
+    # sizes of the C structs on x86-64 (int32 fields, 8-byte pointers/int64)
+    assert ctypes.sizeof(binding.Config) == 24
+    assert ctypes.sizeof(binding.Inputs) == 8 + 8 + 8 + 8 + 8 + 8 + 8 + 8 + 8 + 8
+    assert ctypes.sizeof(binding.Outputs) == 48
+
+
+def test_null_arguments_rejected_without_device():
+    lib = binding.load_library()
+    assert lib.specverify_run(None, None, None, None) == binding.ERR_INVALID_ARGUMENT
+    assert lib.specverify_destroy(None) == binding.OK
+    assert lib.specverify_chunks_per_row(None) == 0
+    h = ctypes.c_void_p()
+    assert lib.specverify_create(None, ctypes.byref(h)) == binding.ERR_INVALID_ARGUMENT
+    bad = binding.Config(0, 4, 1000, binding.BF16, 0, 0)          # max_batch 0
+    assert lib.specverify_create(ctypes.byref(bad), ctypes.byref(h)) == binding.ERR_INVALID_ARGUMENT
+    assert not h.value
+    bad = binding.Config(1, 4, 1000, 7, 0, 0)                      # unknown dtype
+    assert lib.specverify_create(ctypes.byref(bad), ctypes.byref(h)) == binding.ERR_INVALID_ARGUMENT
+    bad = binding.Config(1, 4, 524288 + 1, binding.F32, 0, 0)      # more than 64 chunks
+    assert lib.specverify_create(ctypes.byref(bad), ctypes.byref(h)) == binding.ERR_UNSUPPORTED
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.load_library(str(tmp_path / "nope.so"))

@@ -1,0 +1,314 @@
+"""GPU parity: the HIP verifier against the float64 oracle on seeded inputs.
+
+Every test calls the C ABI through the ctypes binding on cuda:0 and compares
+element by element with the oracle (rules in tests/parity.py).
+"""
+import numpy as np
+import pytest
+
+from rejection_sampling_verifier_specverify_amd.binding import (
+    ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, SpecVerify, SpecVerifyError)
+from rejection_sampling_verifier_specverify_amd.workloads import (
+    WORKLOADS, Workload, make_custom, make_inputs)
+
+from parity import alloc_outputs, compare, fetch, gpu_run, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _handle(inp, **kw):
+    g = int(np.max(inp.gammas)) if inp.batch else 0
+    return SpecVerify(max_batch=max(inp.batch, 1), max_gamma=max(g, 1), vocab=inp.workload.vocab,
+                      dtype=inp.workload.dtype, **kw)
+
+
+def _check(inp, sequences=None, ragged=None, label=""):
+    print(f"[parity] {label} B={inp.batch} V={inp.workload.vocab} dtype={inp.workload.dtype} "
+          f"rows={inp.target.shape[0]}+{inp.draft.shape[0]}", flush=True)
+    sv = _handle(inp)
+    dev = to_device(inp)
+    out = alloc_outputs(inp)
+    gpu_run(sv, dev, out, inp, ragged=ragged)
+    got = fetch(out)
+    rep = compare(inp, got, sequences)
+    print(f"[parity] {label}: {rep.summary()}", flush=True)
+    assert rep.ok(), rep.summary()
+    return rep, got
+
+
+@pytest.mark.parametrize("name,batch", [
+    ("b1_g4_v32000_f32", 1),
+    ("b64_g4_v128256_bf16", 6),
+    ("b256_g8_v128256_bf16_mixedT", 12),
+    ("b32_g1_v129280_bf16_mtp", 10),
+    ("b512_gragged1to7_v152064_bf16", 12),
+])
+def test_small_batches_every_sequence(name, batch):
+    inp = make_inputs(name, seed=0, batch=batch)
+    rep, _ = _check(inp, label=f"{name}[:{batch}]")
+    assert rep.checked == batch
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_seeds_small(seed):
+    for name, batch in (("b1_g4_v32000_f32", 1), ("b32_g1_v129280_bf16_mtp", 8)):
+        _check(make_inputs(name, seed=seed, batch=batch), label=f"{name} seed={seed}")
+
+
+def test_headline_full_size_every_sequence():
+    """B=64, gamma=4, V=128256, bf16: the benchmarked configuration, all 64 sequences."""
+    inp = make_inputs("b64_g4_v128256_bf16", seed=0)
+    rep, got = _check(inp, label="headline full")
+    assert rep.checked == 64
+    assert rep.exact >= 60
+
+
+def test_mtp_full_size_every_sequence():
+    _check(make_inputs("b32_g1_v129280_bf16_mtp", seed=0), label="mtp full")
+
+
+@pytest.mark.parametrize("name", ["b256_g8_v128256_bf16_mixedT", "b512_gragged1to7_v152064_bf16"])
+def test_large_full_size_sampled_sequences(name):
+    """Full batch on the GPU; the oracle checks a spread of sequences one by one."""
+    inp = make_inputs(name, seed=0)
+    B = inp.batch
+    seqs = sorted(set(np.linspace(0, B - 1, 20).astype(int).tolist()) | {0, B - 1})
+    _check(inp, sequences=seqs, label=f"{name} full (sampled {len(seqs)})")
+
+
+# ------------------------------------------------------------------ edge cases
+
+def _rand_custom(V, gammas, T, seed, dtype="bf16", draft_noise=0.5, scale=2.0):
+    rng = np.random.default_rng(seed)
+    R_d = int(np.sum(gammas))
+    R_t = R_d + len(gammas)
+    tgt = rng.normal(size=(R_t, V)) * scale
+    pair = np.concatenate([np.arange(int(np.sum(gammas[:b])), int(np.sum(gammas[:b + 1]))) + b
+                           for b in range(len(gammas))]).astype(int) if R_d else np.zeros(0, int)
+    drf = tgt[pair] + rng.normal(size=(R_d, V)) * draft_noise if R_d else np.zeros((0, V))
+    toks = np.array([int(np.argmax(drf[k] / max(T[0], 1e-3) + rng.gumbel(size=V))) for k in range(R_d)],
+                    dtype=np.int32)
+    u = rng.random(R_t).astype(np.float32)
+    return make_custom(tgt, drf, toks, u, T, gammas, dtype=dtype)
+
+
+@pytest.mark.parametrize("V", [1, 5, 63, 1000, 8191, 8192, 8193, 16384, 20007])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_vocab_sizes_and_tails(V, dtype):
+    gam = [3, 0, 2, 4]
+    inp = _rand_custom(V, gam, [0.9] * 4, seed=V, dtype=dtype)
+    _check(inp, label=f"V={V} {dtype}")
+
+
+def test_max_vocab_64_chunks():
+    inp = _rand_custom(524288, [2, 1], [1.0, 0.5], seed=9)
+    _check(inp, label="V=524288")
+
+
+def test_ragged_with_zero_drafts_and_uniform_form_agree():
+    gam = [0, 3, 7, 1, 0, 5, 2, 6]
+    inp = _rand_custom(30000, gam, [1.0] * 8, seed=4)
+    _check(inp, label="ragged with zeros")
+    uni = _rand_custom(30000, [3] * 5, [0.8] * 5, seed=5)
+    _, a = _check(uni, ragged=False, label="uniform form")
+    _, b = _check(uni, ragged=True, label="ragged form of a uniform batch")
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+def test_gamma_zero_plain_sampling():
+    inp = _rand_custom(50000, [0] * 16, [0.7] * 16, seed=6)
+    rep, _ = _check(inp, label="gamma=0")
+    assert rep.checked == 16
+
+
+def test_equal_distributions_accept_everything():
+    rng = np.random.default_rng(12)
+    V, gam = 20000, [4, 4, 4]
+    tgt = rng.normal(size=(15, V)) * 2
+    pair = [0, 1, 2, 3, 5, 6, 7, 8, 10, 11, 12, 13]
+    toks = rng.integers(0, V, size=12)
+    u = rng.random(15).astype(np.float32)
+    u[[0, 1, 2, 3]] = np.float32(0.99999994)
+    inp = make_custom(tgt, tgt[pair], toks, u, [1.0, 0.6, 2.0], gam)
+    rep, got = _check(inp, label="p == q")
+    assert np.all(got["accepted_len"] == 4)
+    np.testing.assert_allclose(got["beta"], 1.0, atol=1e-5)
+    np.testing.assert_allclose(got["resid_mass"], 0.0, atol=1e-6)
+
+
+def test_disjoint_support_rejects_at_zero():
+    rng = np.random.default_rng(13)
+    V = 12000
+    tgt = rng.normal(size=(3, V))
+    drf = rng.normal(size=(2, V))
+    tgt[0, V // 2:] = -np.inf
+    drf[0, : V // 2] = -np.inf
+    toks = [V // 2 + 17, 3]
+    for u0 in (0.0, 0.5):
+        inp = make_custom(tgt, drf, toks, [u0, 0.1, 0.37], [1.0], [2])
+        rep, got = _check(inp, label=f"disjoint u0={u0}")
+        assert got["accepted_len"][0] == 0 and got["out_tokens"][0] < V // 2
+        assert got["beta"][0] == 0.0 and got["p_draft"][0] == 0.0
+
+
+def test_greedy_ties_and_mixed_temperatures():
+    rng = np.random.default_rng(14)
+    V, gam = 9000, [5, 5, 5, 5, 5, 5]
+    R_t = 36
+    tgt = np.round(rng.normal(size=(R_t, V)) * 2, 0)      # many exact ties at the max
+    pair = [r for b in range(6) for r in range(b * 6, b * 6 + 5)]
+    drf = np.round(tgt[pair] + rng.normal(size=(30, V)) * 0.3, 0)
+    am = np.argmax(tgt[pair], axis=1)
+    toks = np.where(rng.random(30) < 0.8, am, rng.integers(0, V, 30)).astype(np.int32)
+    inp = make_custom(tgt, drf, toks, rng.random(R_t), [0.0, 0.0, 0.6, 0.0, 1.0, 0.0], gam)
+    rep, _ = _check(inp, label="greedy ties")
+    assert rep.greedy == 4
+
+
+def test_one_hot_rows_zero_residual_fallback():
+    V, gam = 40000, [3, 3]
+    tgt = np.full((8, V), -400.0)
+    drf = np.full((6, V), -300.0)
+    for rr in range(8):
+        tgt[rr, 1000 * rr + 7] = 0.0
+    pair = [0, 1, 2, 4, 5, 6]
+    for k, rr in enumerate(pair):
+        drf[k, 1000 * rr + 7] = 0.0
+    toks = [1000 * rr + 7 for rr in pair]
+    toks[1] = 5          # q(5) = e^-300 > p(5) = e^-400: rejected, residual mass 0 -> sample p
+    inp = make_custom(tgt, drf, toks, [0.3] * 8, [1.0, 1.0], gam, dtype="f32")
+    rep, got = _check(inp, label="one-hot fallback")
+    assert got["accepted_len"][0] == 1 and got["out_tokens"][1] == 1007
+    assert got["accepted_len"][1] == 3
+
+
+@pytest.mark.parametrize("case", ["nan", "posinf", "all_neginf", "token", "neg_T", "nan_T", "tiny_T",
+                                  "nan_greedy", "partial_neginf"])
+def test_invalid_data_flagged_per_sequence(case):
+    rng = np.random.default_rng(15)
+    V, gam = 10000, [2, 2, 2]
+    tgt = rng.normal(size=(9, V))
+    drf = rng.normal(size=(6, V))
+    toks = rng.integers(0, V, 6).astype(np.int32)
+    T = [1.0, 1.0, 0.0]
+    if case == "nan":
+        tgt[5, 9999] = np.nan          # bonus row of sequence 1
+    elif case == "posinf":
+        drf[2, 10] = np.inf
+    elif case == "all_neginf":
+        tgt[4, :] = -np.inf
+    elif case == "token":
+        toks[3] = V
+    elif case == "neg_T":
+        T[1] = -1.0
+    elif case == "nan_T":
+        T[1] = float("nan")
+    elif case == "tiny_T":
+        T[1] = 1e-39
+    elif case == "nan_greedy":
+        drf[5, 123] = np.nan
+    elif case == "partial_neginf":
+        tgt[3:6, : V // 2] = -np.inf  # valid: only half the row
+    inp = make_custom(tgt, drf, toks, rng.random(9), T, gam, dtype="f32")
+    rep, got = _check(inp, label=f"invalid {case}")
+    if case == "partial_neginf":
+        assert np.all(got["accepted_len"] >= 0)
+    else:
+        assert rep.invalid == 1
+        bad = 2 if case == "nan_greedy" else 1
+        assert got["accepted_len"][bad] == -1
+        assert np.all(got["out_tokens"][bad * 3: bad * 3 + 3] == -1)
+
+
+def test_repeated_runs_bitwise_identical():
+    """Fixed reduction order: 20 launches on the same buffers give the same bits."""
+    import torch
+    inp = make_inputs("b64_g4_v128256_bf16", seed=3, batch=16)
+    sv = _handle(inp)
+    dev = to_device(inp)
+    ref = None
+    for k in range(20):
+        out = alloc_outputs(inp)
+        gpu_run(sv, dev, out, inp)
+        got = fetch(out)
+        if ref is None:
+            ref = got
+        for name in ref:
+            assert np.array_equal(got[name].view(np.uint32), ref[name].view(np.uint32)), (k, name)
+
+
+def test_back_to_back_runs_on_one_stream_do_not_interfere():
+    """Different batches launched back to back on one handle (epoch-tagged slots)."""
+    a = make_inputs("b32_g1_v129280_bf16_mtp", seed=0, batch=12)
+    b = make_inputs("b32_g1_v129280_bf16_mtp", seed=7, batch=5)
+    sv = _handle(a)
+    da, db = to_device(a), to_device(b)
+    oa, ob = alloc_outputs(a), alloc_outputs(b)
+    for _ in range(3):
+        gpu_run(sv, da, oa, a)
+        gpu_run(sv, db, ob, b)
+    ga, gb = fetch(oa), fetch(ob)
+    assert compare(a, ga).ok() and compare(b, gb).ok()
+
+
+def test_tiny_spin_limit_terminates_with_status():
+    """A one-poll budget forces expired waits from the host: every sequence is either
+    correct or reports -2, and the kernel ends."""
+    inp = make_inputs("b64_g4_v128256_bf16", seed=0, batch=24)
+    sv = _handle(inp, spin_limit=1)
+    dev = to_device(inp)
+    out = alloc_outputs(inp)
+    gpu_run(sv, dev, out, inp)
+    got = fetch(out)
+    ok = SpecVerify(24, 4, inp.workload.vocab, "bf16")
+    out2 = alloc_outputs(inp)
+    gpu_run(ok, dev, out2, inp)
+    ref = fetch(out2)
+    cu = inp.cu_t
+    for b in range(inp.batch):
+        if got["accepted_len"][b] == -2:
+            assert np.all(got["out_tokens"][cu[b]:cu[b + 1]] == -1)
+        else:
+            assert got["accepted_len"][b] == ref["accepted_len"][b]
+            assert np.array_equal(got["out_tokens"][cu[b]:cu[b + 1]], ref["out_tokens"][cu[b]:cu[b + 1]])
+
+
+def test_host_validation_errors():
+    import torch
+    inp = make_inputs("b1_g4_v32000_f32", seed=0)
+    sv = SpecVerify(max_batch=2, max_gamma=4, vocab=32000, dtype="f32")
+    dev = to_device(inp)
+    out = alloc_outputs(inp)
+    with pytest.raises(SpecVerifyError) as e:      # gamma beyond the handle's limit
+        sv.run(dev["target"], dev["draft"], dev["draft_tokens"], dev["uniforms"], dev["temperatures"],
+               gamma=5, **out)
+    assert e.value.status == ERR_INVALID_ARGUMENT
+    with pytest.raises(SpecVerifyError) as e:      # logits not aligned to their element size
+        raw = torch.zeros(5 * 32000 * 4 + 4, dtype=torch.uint8, device="cuda:0")
+        lib = __import__("rejection_sampling_verifier_specverify_amd.binding", fromlist=["x"])
+        inp_c = lib.Inputs(1, 4, None, 4, raw.data_ptr() + 1, 32000, dev["draft"].data_ptr(), 32000,
+                           dev["draft_tokens"].data_ptr(), dev["uniforms"].data_ptr(),
+                           dev["temperatures"].data_ptr())
+        out_c = lib.Outputs(out["accepted_len"].data_ptr(), out["out_tokens"].data_ptr(), None, None, None, None)
+        lib.specverify_run(sv.handle, inp_c, out_c, torch.cuda.current_stream().cuda_stream)
+    assert e.value.status == ERR_UNSUPPORTED
+    # a row stride that breaks 16-byte alignment is accepted (element-wise loads)
+    padded = torch.zeros(5, 32003, device="cuda:0")
+    padded[:, :32000] = dev["target"]
+    dpad = torch.zeros(4, 32001, device="cuda:0")
+    dpad[:, :32000] = dev["draft"]
+    out2 = alloc_outputs(inp)
+    sv.run(padded[:, :32000], dpad[:, :32000], dev["draft_tokens"], dev["uniforms"], dev["temperatures"],
+           gamma=4, **out2)
+    out3 = alloc_outputs(inp)
+    sv.run(dev["target"], dev["draft"], dev["draft_tokens"], dev["uniforms"], dev["temperatures"],
+           gamma=4, **out3)
+    a, b = fetch(out2), fetch(out3)
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+    with pytest.raises(SpecVerifyError):
+        SpecVerify(max_batch=0, max_gamma=4, vocab=32000, dtype="f32")
+    with pytest.raises(SpecVerifyError) as e:
+        SpecVerify(max_batch=1, max_gamma=1, vocab=524289, dtype="f32")
+    assert e.value.status == ERR_UNSUPPORTED
