@@ -1,4 +1,4 @@
-// HIP kernels and C ABI of the speculative-decoding verification sampler,
+// HIP kernel and C ABI of the speculative-decoding verification sampler,
 // written for AMD CDNA4 (gfx950, MI355X).
 //
 // What is computed (velog "6-1편. Speculative Decoding", section 2
@@ -8,38 +8,43 @@
 // include/specverify.h.
 //
 // How.  The logits are read from HBM exactly once.  Every target row is
-// split into chunks of 8192 logits; one 256-thread workgroup owns one chunk
-// of one target row and, when the row has a draft, the same chunk of the
-// draft row, so p_k and q_k of the same token meet in the same registers.
-// Workgroup (row r, chunk c) is blockIdx r * C + c.
+// split into chunks of 8192 logits.  A work item is one chunk of one target
+// row plus, when the position has a draft, the same chunk of the draft row,
+// so p_k and q_k of the same token meet in the same registers.
 //
-//   phase 1   16-byte coalesced loads -> fp32 registers; chunk max m_c; the
-//             exponentials e_k = 2^(l_k * s - m_c * s), s = log2(e) / T,
-//             kept in registers; chunk sum s_c.  T = 0: chunk argmax.
-//   xch 1     (m_c, s_c) of target and draft are published in epoch-tagged
-//             64-bit slots; the chunks of a row that need the row's
-//             normalisers poll the row's slots until every tag carries this
-//             run's epoch.  The merge (max, sum * 2^((m_c - M) s)) is the
-//             associative combine of an online softmax.
-//   phase 2   p_k = e_k * 2^((m_c - M_t) s) / S_t, q_k likewise; the chunk
-//             sums of min(p, q) (beta, velog section 2-3 item 1) and of
-//             w_k = max(0, p_k - q_k) (the residual mass, section 2-3 item 2),
-//             plus the sums of w over 32-lane sub-chunks, are published.
-//   finish    the last chunk of each row: residual mass Z, beta; inverse CDF
-//             of u_gamma * Z over chunk totals -> sub-chunk totals -> the
-//             256 or 128 logits of one sub-chunk, re-read and scanned; the
-//             acceptance test u_i * q(x) < p(x); diagnostics; the row
-//             result in a tagged slot; an arrival on the sequence counter.
-//   resolve   the last row of a sequence to arrive finds the first rejection
-//             n and writes accepted_len and the n + 1 tokens; no host sync.
+// Schedule.  The kernel is persistent: the host launches as many 256-thread
+// workgroups as the GPU holds at once.  Rows are dealt round robin to eight
+// groups that match the eight XCDs (workgroup b runs on XCD b % 8); inside a
+// group, workgroup j takes items j, j + G, j + 2G, ... of the group's
+// row-major item list, so the chunks of a row run together, in one round,
+// on one XCD.  While a workgroup works on one item, the 16-byte loads of its
+// next item are already in flight (double buffering in registers).
 //
-// Synchronisation uses no fences: every value crossing workgroups travels in
-// its own 64-bit slot together with a 32-bit epoch tag, written and read
-// with agent-scope atomics, so a reader that sees the tag sees the value.
-// Every wait is bounded by a poll budget; an expired wait is reported as
-// accepted_len = -2 and the kernel still ends.  Waits only target chunks of
-// the same row (consecutive blockIdx), which the in-order dispatch of each
-// XCD brings up together.
+//   phase 1   chunk max m_c; e_k = 2^(l_k s - m_c s), s = log2(e) / T, kept
+//             in registers; chunk sum s_c.  T = 0: chunk argmax.
+//   xch 1     (m_c, s_c) of target and draft go into epoch-tagged slots; the
+//             row's chunks read all of them and merge (max, sum 2^((m_c-M)s)),
+//             the associative combine of an online softmax.
+//   phase 2   with a_c = 2^((m_c - M) s) / S for target (t) and draft (d) and
+//             rho = a_d / a_t: p_k = a_t e_t and q_k = a_t rho e_d, so
+//             min(p, q) = a_t min(e_t, rho e_d) and max(0, p - q) =
+//             a_t max(0, e_t - rho e_d); the chunk sums of both go out (beta,
+//             velog section 2-3 item 1, and the residual mass Z, item 2), and
+//             the chunk holding the drafted token publishes p(x) and q(x).
+//   xch 2     every chunk of the row reads every chunk's sums: Z, beta and
+//             the chunk whose CDF interval holds u_gamma * Z (or, for the
+//             bonus row and for Z = 0, the CDF of p).
+//   owner     that chunk finds the token in its registers (block scan), runs
+//             the acceptance test u_i q(x) < p(x), writes the diagnostics and
+//             the row result, and counts the row in on its sequence.
+//   resolve   the last row of a sequence finds the first rejection n and
+//             writes accepted_len and the n + 1 tokens; no host sync.
+//
+// Synchronisation uses no fences: every value that crosses workgroups
+// travels in its own 64-bit slot together with a 32-bit epoch tag, written
+// and read with agent-scope atomics, so a reader that sees the tag sees the
+// value.  Every wait is bounded by a poll budget; an expired wait is
+// reported as accepted_len = -2 and the kernel still ends.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -55,13 +60,13 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kPerThread = 32;                 // logits per thread per row
 constexpr int kChunk = kThreads * kPerThread;  // 8192 logits per chunk
 constexpr int kMaxChunks = 64;                 // V <= 524288
-constexpr int kHalf = 32;                      // lanes per sub-chunk
+constexpr int kGroups = 8;                     // row groups = XCDs of an MI355X
 constexpr int kX1 = 4;                         // exchange-1 slots per chunk
-constexpr int kX2Head = 2;                     // exchange-2: W_c, B_c, then sub-totals
-constexpr int kMaxSub = 64;                    // sub-chunks per chunk (f32: 64, bf16: 32)
-constexpr int kDefaultSpin = 1 << 18;   // ~0.3 s of polling; normal waits are microseconds
+constexpr int kX2 = 2;                         // exchange-2 slots per chunk (+2 per row)
+constexpr int kDefaultSpin = 1 << 18;          // ~0.3 s of polling; normal waits are microseconds
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFltMin = 1.17549435e-38f;
+constexpr float kFltMax = 3.40282347e38f;
 constexpr uint32_t kTokMask = (1u << 23) - 1;
 constexpr uint32_t kAccBit = 1u << 23;
 constexpr uint32_t kStatusShift = 24;          // 0 ok, 1 invalid data, 2 wait expired
@@ -92,14 +97,16 @@ struct Params {
   int32_t gamma;
   int32_t B;
   int32_t R_d;
+  int32_t R_t;
   int32_t V;
   int32_t C;                 // chunks per row
+  int32_t G;                 // workgroups per row group
   uint32_t epoch;
   int32_t spin_limit;
-  bool t_aligned;            // target rows start on 16-byte boundaries
-  bool d_aligned;
+  int32_t t_aligned;         // target rows start on 16-byte boundaries
+  int32_t d_aligned;
   uint64_t* xch1;            // [rows][C][kX1]
-  uint64_t* xch2;            // [rows][C][kX2Head + NSUB]
+  uint64_t* xch2;            // [rows][C * kX2 + 2]
   uint64_t* rowslot;         // [rows]
   uint64_t* seqctr;          // [max_batch]
   int32_t* acc_len;
@@ -115,7 +122,9 @@ struct Params {
 __device__ __forceinline__ void slot_put(uint64_t* p, uint32_t tag, uint32_t v) {
   __hip_atomic_store(p, ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
+__device__ __forceinline__ void slot_putf(uint64_t* p, uint32_t tag, float v) {
+  slot_put(p, tag, __float_as_uint(v));
+}
 // Poll one slot until it carries `tag`; false once `limit` polls have failed.
 __device__ __forceinline__ bool slot_get(uint64_t* p, uint32_t tag, int limit, uint32_t& v) {
   for (int k = 0;; ++k) {
@@ -125,38 +134,65 @@ __device__ __forceinline__ bool slot_get(uint64_t* p, uint32_t tag, int limit, u
       return true;
     }
     if (k >= limit) return false;
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(1);
   }
 }
 
-// ------------------------------------------------------------------ reductions
-// Butterflies leave the same value in every lane (addition and max are
-// commutative), so every workgroup that reduces the same data gets the same
-// bits.
+// ------------------------------------------------------------------ wave primitives (DPP)
+// Reductions leave the same value in every lane and use a fixed order, so
+// every workgroup that reduces the same data gets the same bits.
 
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);   // row_half_mirror
+  v += dpp<0x140>(v);   // row_mirror: every lane holds its 16-lane row sum
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
-__device__ __forceinline__ float half_sum(float v) {  // within each 32-lane half
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
-// Inclusive prefix sum over the 64 lanes of a wave, fixed association.
+// Inclusive prefix sum over the 64 lanes, fixed association.
 __device__ __forceinline__ float wave_scan(float v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const float t = __shfl_up(v, d);
-    if (lane >= d) v += t;
-  }
-  return v;
+  v += dpp<0x111>(v);   // row_shr:1 (bound_ctrl: 0 enters at the row start)
+  v += dpp<0x112>(v);   // row_shr:2
+  v += dpp<0x114>(v);   // row_shr:4
+  v += dpp<0x118>(v);   // row_shr:8
+  const float t0 = lane_f(v, 15), t1 = lane_f(v, 31), t2 = lane_f(v, 47);
+  const int row = lane >> 4;
+  const float off = row == 0 ? 0.0f : row == 1 ? t0 : row == 2 ? (t0 + t1) : ((t0 + t1) + t2);
+  return v + off;
+}
+template <int CTRL>
+__device__ __forceinline__ int dppi(int v, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dppi<0xB1>(v, v));
+  v = min(v, dppi<0x4E>(v, v));
+  v = min(v, dppi<0x141>(v, v));
+  v = min(v, dppi<0x140>(v, v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, dppi<0xB1>(v, v));
+  v = max(v, dppi<0x4E>(v, v));
+  v = max(v, dppi<0x141>(v, v));
+  v = max(v, dppi<0x140>(v, v));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 // (value, index): larger value wins, lower index on ties.
 __device__ __forceinline__ void argmax_merge(float& v, int& k, float v2, int k2) {
@@ -165,54 +201,68 @@ __device__ __forceinline__ void argmax_merge(float& v, int& k, float v2, int k2)
     k = k2;
   }
 }
-__device__ __forceinline__ void wave_argmax(float& v, int& k) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float v2 = __shfl_xor(v, m);
-    const int k2 = __shfl_xor(k, m);
-    argmax_merge(v, k, v2, k2);
-  }
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& k) {
+  const float v2 = __int_as_float(dppi<CTRL>(__float_as_int(v), __float_as_int(v)));
+  const int k2 = dppi<CTRL>(k, k);
+  argmax_merge(v, k, v2, k2);
 }
-__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ void wave_argmax(float& v, int& k) {
+  argmax_step<0xB1>(v, k);
+  argmax_step<0x4E>(v, k);
+  argmax_step<0x141>(v, k);
+  argmax_step<0x140>(v, k);   // every lane holds its row's (max, first index)
+  float bv = lane_f(v, 0);
+  int bk = __builtin_amdgcn_readlane(k, 0);
+#pragma unroll
+  for (int l = 16; l < 64; l += 16)
+    argmax_merge(bv, bk, lane_f(v, l), __builtin_amdgcn_readlane(k, l));
+  v = bv;
+  k = bk;
+}
 
 // ------------------------------------------------------------------ loads
 
-// Load this thread's 32 logits of a chunk as fp32.  Element x[u*EPV + e] is
-// token e0 + u*256*EPV + tid*EPV + e; tokens >= V read as -inf.
+// Issue this thread's loads of one chunk row: vector u holds tokens
+// e0 + u*256*EPV + tid*EPV .. +EPV-1.  Tokens >= V read as -inf; rows not on
+// 16-byte boundaries are read element by element.
 template <int DT>
-__device__ __forceinline__ void load_chunk(const void* base, int64_t row, int64_t stride,
-                                           int64_t e0, int V, int tid, bool aligned,
-                                           float (&x)[kPerThread]) {
+__device__ __forceinline__ void issue_chunk(const void* base, int64_t row, int64_t stride, int64_t e0,
+                                            int V, int tid, bool aligned, u32x4 (&raw)[Fmt<DT>::U]) {
   using F = Fmt<DT>;
   const char* rowp = (const char*)base + row * stride * F::ESIZE;
-  u32x4 raw[F::U];
   if (aligned && e0 + kChunk <= V) {
 #pragma unroll
     for (int u = 0; u < F::U; ++u) {
       const int64_t k = e0 + (int64_t)u * kThreads * F::EPV + (int64_t)tid * F::EPV;
       raw[u] = __builtin_nontemporal_load((const u32x4*)(rowp + k * F::ESIZE));
     }
-  } else {
+    return;
+  }
 #pragma unroll
-    for (int u = 0; u < F::U; ++u) {
-      const int64_t k = e0 + (int64_t)u * kThreads * F::EPV + (int64_t)tid * F::EPV;
-      if (aligned && k + F::EPV <= V) {
-        raw[u] = __builtin_nontemporal_load((const u32x4*)(rowp + k * F::ESIZE));
-      } else if (DT == SPECVERIFY_F32) {
-        const uint32_t* p = (const uint32_t*)rowp;
+  for (int u = 0; u < F::U; ++u) {
+    const int64_t k = e0 + (int64_t)u * kThreads * F::EPV + (int64_t)tid * F::EPV;
+    if (aligned && k + F::EPV <= V) {
+      raw[u] = __builtin_nontemporal_load((const u32x4*)(rowp + k * F::ESIZE));
+    } else if (DT == SPECVERIFY_F32) {
+      const uint32_t* p = (const uint32_t*)rowp;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) raw[u][e] = (k + e < V) ? p[k + e] : 0xFF800000u;
-      } else {
-        const uint16_t* p = (const uint16_t*)rowp;
+      for (int e = 0; e < 4; ++e) raw[u][e] = (k + e < V) ? p[k + e] : 0xFF800000u;
+    } else {
+      const uint16_t* p = (const uint16_t*)rowp;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (k + 2 * e < V) ? p[k + 2 * e] : 0xFF80u;
-          const uint32_t hi = (k + 2 * e + 1 < V) ? p[k + 2 * e + 1] : 0xFF80u;
-          raw[u][e] = lo | (hi << 16);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (k + 2 * e < V) ? p[k + 2 * e] : 0xFF80u;
+        const uint32_t hi = (k + 2 * e + 1 < V) ? p[k + 2 * e + 1] : 0xFF80u;
+        raw[u][e] = lo | (hi << 16);
       }
     }
   }
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack(const u32x4 (&raw)[Fmt<DT>::U], float (&x)[kPerThread]) {
+  using F = Fmt<DT>;
 #pragma unroll
   for (int u = 0; u < F::U; ++u) {
 #pragma unroll
@@ -228,38 +278,81 @@ __device__ __forceinline__ void load_chunk(const void* base, int64_t row, int64_
   }
 }
 
-template <int DT>
-__device__ __forceinline__ float load_one(const void* base, int64_t row, int64_t stride, int64_t k) {
-  if (DT == SPECVERIFY_F32) return ((const float*)base)[row * stride + k];
-  const uint16_t b = ((const uint16_t*)base)[row * stride + k];
-  return __uint_as_float((uint32_t)b << 16);
-}
-
-// Residual weight max(0, p - q) of one logit from its exponentials and the
-// chunk scales; phase 2 and the finisher's re-scan both use this, so that
-// (built without fp contraction) they produce the same bits.
-__device__ __forceinline__ float resid_weight(float et, float at, float ed, float ad) {
-  const float p = et * at;
-  const float q = ed * ad;
-  return fmaxf(p - q, 0.0f);
-}
-
-// Exponent offset of a chunk: -m * s, or 0 for a chunk of only -inf (so that
+// Exponent offset of a chunk: -m s, or 0 for a chunk of only -inf (so that
 // its exponentials are 2^-inf = 0 instead of NaN).
 __device__ __forceinline__ float chunk_offset(float m, float s) {
   return (m == -__builtin_huge_valf()) ? 0.0f : -m * s;
 }
 
+// ------------------------------------------------------------------ work items
+
+struct Item {
+  int r;       // target row
+  int c;       // chunk
+  int b;       // sequence
+  int gam;     // its draft length
+  int d0;      // its first draft row
+  int i;       // position in the sequence (r - cu_t[b])
+  bool ok;     // consistent cu_draft
+  bool pair;   // the position has a draft row
+  float T;     // temperature of the sequence
+  int xtok;    // drafted token (pair rows)
+  float ui;    // acceptance uniform of the position
+  float ug;    // uniform of the sequence's final sample
+};
+
+__device__ __forceinline__ void item_place(const Params& P, int grp, int idx, Item& it) {
+  const int rl = idx / P.C;
+  it.c = idx - rl * P.C;
+  it.r = rl * kGroups + grp;
+}
+
+// Sequence of the item's row, and the per-row scalars (their loads overlap
+// the work on the current item).
+__device__ __forceinline__ void item_lookup(const Params& P, Item& it) {
+  if (P.cu_draft == nullptr) {
+    it.b = it.r / (P.gamma + 1);
+    it.gam = P.gamma;
+    it.d0 = it.b * P.gamma;
+  } else {
+    int lo = 0, hi = P.B - 1;
+    while (lo < hi) {   // largest b with cu_t[b] = cu_draft[b] + b <= r
+      const int mid = (lo + hi + 1) >> 1;
+      if (P.cu_draft[mid] + mid <= it.r) lo = mid;
+      else hi = mid - 1;
+    }
+    it.b = lo;
+    it.d0 = P.cu_draft[it.b];
+    it.gam = P.cu_draft[it.b + 1] - it.d0;
+  }
+  it.i = it.r - (it.d0 + it.b);
+  it.ok = it.gam >= 0 && it.d0 >= 0 && it.d0 + it.gam <= P.R_d && it.i >= 0 && it.i <= it.gam;
+  it.pair = it.ok && it.i < it.gam;
+  it.T = 0.0f;
+  it.xtok = 0;
+  it.ui = 0.0f;
+  it.ug = 0.0f;
+  if (it.ok) {
+    it.T = P.temps[it.b];
+    it.ui = P.uniforms[it.r];
+    it.ug = P.uniforms[it.d0 + it.b + it.gam];
+    if (it.pair) it.xtok = P.tokens[it.d0 + it.i];
+  }
+}
+
+// ------------------------------------------------------------------ shared state
+
 struct Shared {
   float red[2 * kWaves];
   int redi[2 * kWaves];
   uint32_t x1[kX1 * kMaxChunks];     // exchange-1 payloads of the row
-  float tot[kMaxChunks];             // chunk weight totals (W_c or P_c)
-  float btot[kMaxChunks];            // chunk sums of min(p, q)
-  float sub[kMaxSub];                // sub-chunk weight totals of the owner chunk
-  float Mt, St, Md, Sd;              // row normalisers
-  float scal[8];
-  int flag;
+  uint32_t x2[kX2 * kMaxChunks + 2]; // exchange-2 payloads (+ p(x), q(x))
+  float scan[8 * kWaves];            // block scan scratch
+  float Z, beta, thr, before;
+  float Mt, St, Md, Sd;
+  int owner;
+  int mode;
+  int payload;
   int last;
 };
 
@@ -304,6 +397,18 @@ __device__ __forceinline__ void block_argmax(float& v, int& k, Shared& sh) {
   __syncthreads();
 }
 
+// Gather n <= 256 slots starting at base into dst (every thread calls).
+__device__ __forceinline__ bool gather(uint64_t* base, int n, uint32_t tag, int spin, uint32_t* dst) {
+  int ok = 1;
+  const int tid = threadIdx.x;
+  if (tid < n) {
+    uint32_t v = 0;
+    ok = slot_get(base + tid, tag, spin, v);
+    dst[tid] = v;
+  }
+  return __syncthreads_and(ok) != 0;
+}
+
 // Per-thread argmax of a chunk in token order (first maximum wins) plus a
 // flag for NaN / +inf.
 template <int DT>
@@ -311,89 +416,119 @@ __device__ __forceinline__ void thread_argmax(const float (&x)[kPerThread], int6
                                               float& bv, int& bk, int& bad) {
   using F = Fmt<DT>;
   bv = -__builtin_huge_valf();
-  bk = 0x7FFFFFFF;
+  int slot = -1;   // u * EPV + e of the best logit so far
 #pragma unroll
-  for (int u = 0; u < F::U; ++u) {
-#pragma unroll
-    for (int e = 0; e < F::EPV; ++e) {
-      const float v = x[u * F::EPV + e];
-      bad |= (v != v) | (v == __builtin_huge_valf());
-      if (v > bv) {
-        bv = v;
-        bk = (int)(e0 + (int64_t)u * kThreads * F::EPV + (int64_t)tid * F::EPV + e);
-      }
+  for (int k = 0; k < kPerThread; ++k) {
+    const float v = x[k];
+    bad |= (v != v) | (v == __builtin_huge_valf());
+    if (v > bv) {
+      bv = v;
+      slot = k;
     }
   }
+  const int u = slot / F::EPV, e = slot - u * F::EPV;
+  bk = slot < 0 ? 0x7FFFFFFF : (int)(e0 + u * (kThreads * F::EPV) + tid * F::EPV + e);
 }
 
-// Inverse CDF inside one sub-chunk (wave 0 only; lanes 0..31 own EPV logits
-// each).  w: this lane's weights; base: CDF value before the sub-chunk; thr:
-// u * Z.  Returns the sub-chunk-local index of the first logit with w > 0 and
-// base + C_k > thr, else of the last logit with w > 0 (rounding guard).
-template <int EPV>
-__device__ __forceinline__ int subchunk_search(const float (&w)[EPV], float base, float thr, int lane) {
-  float loc[EPV];
-  float run = 0.0f;
-#pragma unroll
-  for (int e = 0; e < EPV; ++e) {
-    run += w[e];
-    loc[e] = run;
-  }
-  const float lane_tot = lane < kHalf ? run : 0.0f;
-  const float incl = wave_scan(lane_tot, lane);
-  float excl = __shfl_up(incl, 1);
-  if (lane == 0) excl = 0.0f;
-  int first = 0x7FFFFFFF, lastpos = -1;
-  if (lane < kHalf) {
-#pragma unroll
-    for (int e = EPV - 1; e >= 0; --e) {
-      const float Ck = base + (excl + loc[e]);
-      if (w[e] > 0.0f && Ck > thr) first = lane * EPV + e;
-    }
-#pragma unroll
-    for (int e = 0; e < EPV; ++e)
-      if (w[e] > 0.0f) lastpos = lane * EPV + e;
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    first = min(first, __shfl_xor(first, m));
-    lastpos = max(lastpos, __shfl_xor(lastpos, m));
-  }
-  return first != 0x7FFFFFFF ? first : lastpos;
-}
-
-// Owner selection over n <= 64 non-negative totals held one per lane (wave 0):
-// first j with tot_j > 0 and base + incl_j > thr, else the last j with
-// tot_j > 0.  Returns j (or -1 if every total is 0) and the CDF value before j.
-__device__ __forceinline__ int owner_select(float tot, int n, float base, float thr, int lane,
-                                            float& before) {
+// Owner selection over n <= 64 non-negative chunk totals, one per lane of
+// wave 0: the first j with tot_j > 0 and incl_j > thr, else the last j with
+// tot_j > 0 (rounding guard).  Returns j (-1 if all are 0) and the CDF value
+// before j.
+__device__ __forceinline__ int owner_select(float tot, int n, float thr, int lane, float& before) {
   const float t = lane < n ? tot : 0.0f;
   const float incl = wave_scan(t, lane);
-  const float G = base + incl;
-  const uint64_t hit = wave_ballot(lane < n && t > 0.0f && G > thr);
-  const uint64_t pos = wave_ballot(lane < n && t > 0.0f);
+  const uint64_t hit = __ballot(lane < n && t > 0.0f && incl > thr);
+  const uint64_t pos = __ballot(lane < n && t > 0.0f);
   int j;
   if (hit) j = __builtin_ctzll(hit);
   else if (pos) j = 63 - __builtin_clzll(pos);
   else j = -1;
-  const float prev = __shfl(G, j > 0 ? j - 1 : 0);
-  before = j > 0 ? prev : base;
+  const float prev = __shfl(incl, j > 0 ? j - 1 : 0);
+  before = j > 0 ? prev : 0.0f;
   return j;
 }
 
-// Publish the row result and count the row in on its sequence (thread 0).
-// Returns true for the last of the sequence's gamma + 1 rows to arrive.  The
-// counter word holds (epoch, count); a stale epoch counts as zero, so a run
-// never depends on what earlier runs left behind.
-__device__ __forceinline__ bool arrive(const Params& P, int r, int b, int gam, uint32_t tag,
-                                       uint32_t payload) {
-  slot_put(P.rowslot + r, tag, payload);
+// Inverse CDF inside one chunk held in registers (every thread calls).  w:
+// this thread's weights in the layout of issue_chunk; tau: threshold in the
+// chunk's own units.  Token order is round u, then thread, then element.
+// Returns the chunk-local index of the first logit with w > 0 whose running
+// sum exceeds tau, else of the last logit with w > 0, else -1.
+template <int DT>
+__device__ __forceinline__ int chunk_search(const float (&w)[kPerThread], float tau, Shared& sh) {
+  using F = Fmt<DT>;
+  constexpr int U = F::U, EPV = F::EPV;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  float g[U], incl[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) a += w[u * EPV + e];
+    g[u] = a;
+    incl[u] = wave_scan(a, lane);
+    if (lane == 63) sh.scan[u * kWaves + wv] = incl[u];
+  }
+  __syncthreads();
+  float round_off = 0.0f;   // total of all earlier rounds
+  int cslot = -1, lslot = -1;   // u * EPV + e of this thread's first hit / last positive weight
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float off = round_off;
+    for (int k = 0; k < wv; ++k) off += sh.scan[u * kWaves + k];
+    float run = off + (incl[u] - g[u]);   // exclusive prefix of this thread's group
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const float x = w[u * EPV + e];
+      run += x;
+      if (x > 0.0f) {
+        lslot = u * EPV + e;
+        if (run > tau && cslot < 0) cslot = u * EPV + e;
+      }
+    }
+    float rt = round_off;
+    for (int k = 0; k < kWaves; ++k) rt += sh.scan[u * kWaves + k];
+    round_off = rt;
+  }
+  // token order: round u first, then thread, then element
+  int cand = cslot < 0 ? 0x7FFFFFFF : (cslot / EPV) * (kThreads * EPV) + tid * EPV + cslot % EPV;
+  int lastpos = lslot < 0 ? -1 : (lslot / EPV) * (kThreads * EPV) + tid * EPV + lslot % EPV;
+  cand = wave_min_i(cand);
+  lastpos = wave_max_i(lastpos);
+  __syncthreads();
+  if (lane == 0) {
+    sh.redi[wv] = cand;
+    sh.redi[kWaves + wv] = lastpos;
+  }
+  __syncthreads();
+  int c2 = 0x7FFFFFFF, l2 = -1;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    c2 = min(c2, sh.redi[k]);
+    l2 = max(l2, sh.redi[kWaves + k]);
+  }
+  __syncthreads();
+  return c2 != 0x7FFFFFFF ? c2 : l2;
+}
+
+// ------------------------------------------------------------------ row result and sequence
+
+__device__ __forceinline__ uint32_t row_payload(int status, bool acc, int tok) {
+  return ((uint32_t)status << kStatusShift) | (acc ? kAccBit : 0u) |
+         (status == 0 ? ((uint32_t)tok & kTokMask) : 0u);
+}
+
+// Publish the row result and count the row in on its sequence (one thread).
+// True for the last of the sequence's gamma + 1 rows.  The counter word holds
+// (epoch, count); a stale epoch counts as zero, so no run depends on what
+// earlier runs left behind.
+__device__ __forceinline__ bool arrive(const Params& P, int r, int b, int gam, uint32_t payload) {
+  slot_put(P.rowslot + r, P.epoch, payload);
   uint64_t* ctr = P.seqctr + b;
   uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint32_t cnt = 0;
   for (int k = 0; k < (1 << 20); ++k) {
-    cnt = ((uint32_t)(old >> 32) == tag) ? (uint32_t)old + 1u : 1u;
-    const uint64_t nw = ((uint64_t)tag << 32) | cnt;
+    cnt = ((uint32_t)(old >> 32) == P.epoch) ? (uint32_t)old + 1u : 1u;
+    const uint64_t nw = ((uint64_t)P.epoch << 32) | cnt;
     if (__hip_atomic_compare_exchange_strong(ctr, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT))
       break;
@@ -403,19 +538,16 @@ __device__ __forceinline__ bool arrive(const Params& P, int r, int b, int gam, u
 
 // The last row of sequence b to finish: first rejection n, accepted length
 // and the n + 1 emitted tokens (wave 0).
-__device__ __forceinline__ void resolve(const Params& P, int b, int t0, int d0, int gam, uint32_t tag,
-                                        int lane) {
+__device__ __forceinline__ void resolve(const Params& P, int b, int t0, int d0, int gam, int lane) {
   int n = gam, st = 0;
   for (int j0 = 0; j0 <= gam; j0 += 64) {
     const int j = j0 + lane;
     uint32_t v = 0;
     int okj = 1;
-    if (j <= gam) okj = slot_get(P.rowslot + t0 + j, tag, P.spin_limit, v);
-    int sj = (j <= gam) ? (okj ? (int)(v >> kStatusShift) : 2) : 0;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) sj = max(sj, __shfl_xor(sj, m));
-    st = max(st, sj);
-    const uint64_t rb = wave_ballot(j < gam && !(v & kAccBit));
+    if (j <= gam) okj = slot_get(P.rowslot + t0 + j, P.epoch, P.spin_limit, v);
+    const int sj = (j <= gam) ? (okj ? (int)(v >> kStatusShift) : 2) : 0;
+    st = max(st, wave_max_i(sj));
+    const uint64_t rb = __ballot(j < gam && !(v & kAccBit));
     if (n == gam && rb) n = j0 + __builtin_ctzll(rb);
   }
   uint32_t tn = 0;
@@ -433,34 +565,25 @@ __device__ __forceinline__ void resolve(const Params& P, int b, int t0, int d0, 
   if (lane == 0) P.acc_len[b] = st == 2 ? -2 : st == 1 ? -1 : n;
 }
 
-__device__ __forceinline__ uint32_t row_payload(int status, bool acc, int tok) {
-  return ((uint32_t)status << kStatusShift) | (acc ? kAccBit : 0u) |
-         (status == 0 ? ((uint32_t)tok & kTokMask) : 0u);
-}
-
-// Gather the exchange-1 slots of row r into sh.x1 (every thread calls).
-__device__ __forceinline__ bool gather_x1(uint64_t* x1row, int C, uint32_t tag, int spin, Shared& sh) {
-  int ok = 1;
+// Row result of the workgroup that decides a row: publish, arrive, resolve.
+__device__ __forceinline__ void finish_row(const Params& P, const Item& it, Shared& sh) {
   const int tid = threadIdx.x;
-  if (tid < kX1 * C) {
-    uint32_t v = 0;
-    ok = slot_get(x1row + tid, tag, spin, v);
-    sh.x1[tid] = v;
-  }
-  return __syncthreads_and(ok) != 0;
+  if (tid == 0) sh.last = arrive(P, it.r, it.b, it.gam, (uint32_t)sh.payload) ? 1 : 0;
+  __syncthreads();
+  if (sh.last && tid < 64) resolve(P, it.b, it.d0 + it.b, it.d0, it.gam, tid);
 }
 
-// ---------------------------------------------------------------- greedy rows
+// ------------------------------------------------------------------ greedy rows
 // T = 0 (or an invalid temperature, which only needs the row to be reported):
-// chunk argmax of target and draft, and the finisher's greedy decision.
+// chunk argmax of target and draft; the last chunk decides.
 template <int DT>
-__device__ __forceinline__ void greedy_row(const Params& P, const float (&xt)[kPerThread], const float (&xd)[kPerThread],
-                           int r, int c, int b, int t0, int d0, int gam, int rd, bool pair, bool t_ok,
-                           Shared& sh) {
+__device__ __forceinline__ void greedy_item(const Params& P, const Item& it, const float (&xt)[kPerThread],
+                                            const float (&xd)[kPerThread], bool t_ok, Shared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, C = P.C;
   const uint32_t tag = P.epoch;
-  const int64_t e0 = (int64_t)c * kChunk;
-  uint64_t* x1row = P.xch1 + (int64_t)r * C * kX1;
+  const bool pair = it.pair;
+  const int64_t e0 = (int64_t)it.c * kChunk;
+  uint64_t* x1row = P.xch1 + (int64_t)it.r * C * kX1;
   float vt, vd = -__builtin_huge_valf();
   int kt, kd = 0x7FFFFFFF, badt = 0, badd = 0;
   thread_argmax<DT>(xt, e0, tid, vt, kt, badt);
@@ -469,15 +592,13 @@ __device__ __forceinline__ void greedy_row(const Params& P, const float (&xt)[kP
   badd = __syncthreads_or(badd);
   block_argmax(vt, kt, sh);
   if (pair) block_argmax(vd, kd, sh);
-  if (tid == 0) {
-    uint64_t* s = x1row + (int64_t)c * kX1;
-    slot_put(s + 0, tag, __float_as_uint(vt));
-    slot_put(s + 1, tag, badt ? 0xFFFFFFFFu : (uint32_t)kt);
-    slot_put(s + 2, tag, __float_as_uint(vd));
-    slot_put(s + 3, tag, badd ? 0xFFFFFFFFu : (uint32_t)kd);
+  if (tid < kX1) {
+    const uint32_t v = tid == 0 ? __float_as_uint(vt) : tid == 1 ? (badt ? 0xFFFFFFFFu : (uint32_t)kt)
+                     : tid == 2 ? __float_as_uint(vd) : (badd ? 0xFFFFFFFFu : (uint32_t)kd);
+    slot_put(x1row + (int64_t)it.c * kX1 + tid, tag, v);
   }
-  if (c != C - 1) return;
-  const bool ok = gather_x1(x1row, C, tag, P.spin_limit, sh);
+  if (it.c != C - 1) return;
+  const bool ok = gather(x1row, kX1 * C, tag, P.spin_limit, sh.x1);
   if (tid < 64) {
     float av = -__builtin_huge_valf(), dv = -__builtin_huge_valf();
     int ak = 0x7FFFFFFF, dk = 0x7FFFFFFF, bad = 0;
@@ -496,46 +617,45 @@ __device__ __forceinline__ void greedy_row(const Params& P, const float (&xt)[kP
     if (status == 0 && (!t_ok || bad || av == -__builtin_huge_valf() ||
                         (pair && dv == -__builtin_huge_valf())))
       status = 1;
-    bool acc = false;
-    int x = 0;
-    if (pair) {
-      x = P.tokens[rd];
-      if (status == 0 && (x < 0 || x >= P.V)) status = 1;
-      acc = (x == ak);
-    }
+    const int x = it.xtok;
+    if (pair && status == 0 && (x < 0 || x >= P.V)) status = 1;
+    const bool acc = pair && (x == ak);
     if (lane == 0) {
+      const int rd = it.d0 + it.i;
       if (pair && status == 0) {
         if (P.p_draft) P.p_draft[rd] = (x == ak) ? 1.0f : 0.0f;
         if (P.q_draft) P.q_draft[rd] = (x == dk) ? 1.0f : 0.0f;
         if (P.beta) P.beta[rd] = (ak == dk) ? 1.0f : 0.0f;
         if (P.resid) P.resid[rd] = (ak == dk) ? 0.0f : 1.0f;
       }
-      sh.last = arrive(P, r, b, gam, tag, row_payload(status, acc, ak)) ? 1 : 0;
+      sh.payload = (int)row_payload(status, acc, ak);
     }
   }
   __syncthreads();
-  if (sh.last && tid < 64) resolve(P, b, t0, d0, gam, tag, lane);
+  finish_row(P, it, sh);
 }
 
-// ---------------------------------------------------------------- sampled rows
+// ------------------------------------------------------------------ sampled rows (T > 0)
 template <int DT>
-__device__ __forceinline__ void sampled_row(const Params& P, float (&xt)[kPerThread], float (&xd)[kPerThread], int r,
-                            int c, int b, int t0, int d0, int gam, int rd, bool pair, float T,
-                            Shared& sh) {
+__device__ __forceinline__ void sampled_item(const Params& P, const Item& it, float (&xt)[kPerThread],
+                                             float (&xd)[kPerThread], Shared& sh) {
   using F = Fmt<DT>;
   constexpr int EPV = F::EPV;
   constexpr int U = F::U;
-  constexpr int NSUB = (kThreads / kHalf) * U;
-  constexpr int SLOTS2 = kX2Head + NSUB;
   const int tid = threadIdx.x, lane = tid & 63, C = P.C;
   const uint32_t tag = P.epoch;
   const int spin = P.spin_limit;
-  const bool finisher = (c == C - 1);
-  uint64_t* x1row = P.xch1 + (int64_t)r * C * kX1;
-  const float s = kLog2e / T;
+  const bool pair = it.pair;
+  const int rd = it.d0 + it.i;
+  uint64_t* x1row = P.xch1 + (int64_t)it.r * C * kX1;
+  uint64_t* x2row = P.xch2 + (int64_t)it.r * (C * kX2 + 2);
+  const float s = kLog2e / it.T;
+  const float ninf = -__builtin_huge_valf();
+  const bool tok_ok = !pair || (it.xtok >= 0 && it.xtok < P.V);
+  const int xchunk = (pair && tok_ok) ? it.xtok / kChunk : -1;
 
   // ---- phase 1: chunk max, exponentials kept in registers, chunk sum
-  float mt = -__builtin_huge_valf(), md = -__builtin_huge_valf();
+  float mt = ninf, md = ninf;
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) mt = fmaxf(mt, xt[k]);
   if (pair) {
@@ -577,23 +697,18 @@ __device__ __forceinline__ void sampled_row(const Params& P, float (&xt)[kPerThr
     sd = (a0 + a1) + (a2 + a3);
   }
   block_sum2(st, sd, sh);
-  if (tid == 0) {
-    uint64_t* sl = x1row + (int64_t)c * kX1;
-    slot_put(sl + 0, tag, __float_as_uint(mt));
-    slot_put(sl + 1, tag, __float_as_uint(st));
-    slot_put(sl + 2, tag, __float_as_uint(md));
-    slot_put(sl + 3, tag, __float_as_uint(sd));
+  if (tid < kX1) {
+    const float v = tid == 0 ? mt : tid == 1 ? st : tid == 2 ? md : sd;
+    slot_putf(x1row + (int64_t)it.c * kX1 + tid, tag, v);
   }
-  if (!pair && !finisher) return;   // the other chunks of a bonus row are done
 
   // ---- exchange 1: the row's normalisers (M, S) of target and draft
-  const bool ok = gather_x1(x1row, C, tag, spin, sh);
-  if (!ok && !finisher) return;     // the finisher will time out and report
+  const bool ok = gather(x1row, kX1 * C, tag, spin, sh.x1);
   if (tid < 64) {
     const bool in = lane < C;
-    const float m1 = in ? __uint_as_float(sh.x1[lane * kX1 + 0]) : -__builtin_huge_valf();
+    const float m1 = in ? __uint_as_float(sh.x1[lane * kX1 + 0]) : ninf;
     const float s1 = in ? __uint_as_float(sh.x1[lane * kX1 + 1]) : 0.0f;
-    const float m2 = in ? __uint_as_float(sh.x1[lane * kX1 + 2]) : -__builtin_huge_valf();
+    const float m2 = in ? __uint_as_float(sh.x1[lane * kX1 + 2]) : ninf;
     const float s2 = in ? __uint_as_float(sh.x1[lane * kX1 + 3]) : 0.0f;
     const float Mt = wave_max(m1);
     const float Md = wave_max(m2);
@@ -608,247 +723,178 @@ __device__ __forceinline__ void sampled_row(const Params& P, float (&xt)[kPerThr
   }
   __syncthreads();
   const float Mt = sh.Mt, St = sh.St, Md = sh.Md, Sd = sh.Sd;
-  const float ninf = -__builtin_huge_valf();
   const bool norm_ok = ok && Mt > ninf && St == St && St > 0.0f &&
                        (!pair || (Md > ninf && Sd == Sd && Sd > 0.0f));
+  const float at = __builtin_amdgcn_exp2f((mt - Mt) * s) / St;   // p_k = at e_t
+  const float ad = __builtin_amdgcn_exp2f((md - Md) * s) / Sd;   // q_k = ad e_d
+  const float rho = ad / at;                                     // q_k = at rho e_d
 
-  // ---- phase 2: beta and residual mass of this chunk, plus sub-chunk sums
-  if (pair && ok) {
-    const float at = __builtin_amdgcn_exp2f((mt - Mt) * s) / St;
-    const float ad = __builtin_amdgcn_exp2f((md - Md) * s) / Sd;
-    float bsum = 0.0f, wtot = 0.0f;
-    float wsub[U];
+  // ---- phase 2 (rows with a draft): sums of min(e_t, rho e_d) and max(0, e_t - rho e_d)
+  bool ok2 = true;
+  if (pair) {
+    if (norm_ok) {
+      float bsum = 0.0f, wsum = 0.0f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float ws = 0.0f;
+      for (int u = 0; u < U; ++u) {
+        float ws = 0.0f;
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const float p = xt[u * EPV + e] * at;
-        const float q = xd[u * EPV + e] * ad;
-        bsum += fminf(p, q);
-        ws += resid_weight(xt[u * EPV + e], at, xd[u * EPV + e], ad);
+        for (int e = 0; e < EPV; ++e) {
+          const float et = xt[u * EPV + e];
+          const float qe = rho * xd[u * EPV + e];
+          bsum += fminf(et, qe);
+          ws += fmaxf(et - qe, 0.0f);
+        }
+        wsum += ws;
       }
-      wsub[u] = ws;
-      wtot += ws;
-    }
-    block_sum2(wtot, bsum, sh);
-    uint64_t* x2 = P.xch2 + ((int64_t)r * C + c) * SLOTS2;
+      block_sum2(wsum, bsum, sh);
+      if (tid < kX2) slot_putf(x2row + (int64_t)it.c * kX2 + tid, tag, tid == 0 ? at * wsum : at * bsum);
+      if (it.c == xchunk) {   // the chunk holding the drafted token: p(x), q(x)
+        const int loc = it.xtok - it.c * kChunk;
+        const int u = loc / (kThreads * EPV);
+        const int rem = loc - u * kThreads * EPV;
+        if (tid == rem / EPV) {
+          const int e = rem % EPV;
+          float et = 0.0f, ed = 0.0f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float sub = half_sum(wsub[u]);
-      if ((tid & (kHalf - 1)) == 0)
-        slot_put(x2 + kX2Head + u * (kThreads / kHalf) + tid / kHalf, tag, __float_as_uint(sub));
-    }
-    if (tid == 0) {
-      slot_put(x2 + 0, tag, __float_as_uint(wtot));
-      slot_put(x2 + 1, tag, __float_as_uint(bsum));
-    }
-  }
-  if (!finisher) return;
-
-  // ---------------- finisher: residual mass, beta, inverse CDF, acceptance
-  int status = ok ? 0 : 2;
-  const int xtok = pair ? P.tokens[rd] : 0;
-  float Z = 0.0f, beta = 0.0f;
-  if (pair && status == 0) {
-    int ok2 = 1;
-    if (tid < 2 * C) {
-      uint32_t v = 0;
-      const int cc = tid >> 1;
-      ok2 = slot_get(P.xch2 + ((int64_t)r * C + cc) * SLOTS2 + (tid & 1), tag, spin, v);
-      if (tid & 1) sh.btot[cc] = __uint_as_float(v);
-      else sh.tot[cc] = __uint_as_float(v);
-    }
-    ok2 = __syncthreads_and(ok2);
-    if (tid < 64) {
-      const float wz = wave_sum(lane < C ? sh.tot[lane] : 0.0f);
-      const float bz = wave_sum(lane < C ? sh.btot[lane] : 0.0f);
-      if (lane == 0) {
-        sh.scal[0] = wz;
-        sh.scal[1] = bz;
+          for (int k = 0; k < kPerThread; ++k)
+            if (k == u * EPV + e) {
+              et = xt[k];
+              ed = xd[k];
+            }
+          slot_putf(x2row + C * kX2 + 0, tag, et * at);
+          slot_putf(x2row + C * kX2 + 1, tag, ed * ad);
+        }
       }
     }
-    __syncthreads();
-    Z = sh.scal[0];
-    beta = sh.scal[1];
-    if (!ok2) status = 2;
+    // ---- exchange 2: residual mass, beta, p(x), q(x)
+    const int n2 = norm_ok ? (tok_ok ? kX2 * C + 2 : kX2 * C) : 0;
+    ok2 = gather(x2row, n2, tag, spin, sh.x2);
   }
-  const bool t_ok = T >= kFltMin && T <= 3.40282347e38f;
-  if (status == 0 && (!t_ok || !norm_ok || (pair && (xtok < 0 || xtok >= P.V)))) status = 1;
-  // sampled weights: the residual max(0, p - q) if it has mass, else p
-  // (the bonus row, or Z = 0 where the residual is undefined)
-  const bool resid_mode = pair && Z > 0.0f;
+
+  // ---- which chunk holds the sampled token
+  // weights: the residual max(0, p - q) when it has mass, else p (bonus row,
+  // or Z = 0 where the residual is undefined)
+  if (tid < 64) {
+    float Z = 0.0f, beta = 0.0f;
+    if (pair && norm_ok && ok2) {
+      Z = wave_sum(lane < C ? __uint_as_float(sh.x2[lane * kX2 + 0]) : 0.0f);
+      beta = wave_sum(lane < C ? __uint_as_float(sh.x2[lane * kX2 + 1]) : 0.0f);
+    }
+    const bool resid_mode = pair && Z > 0.0f;
+    float tot;
+    if (resid_mode) {
+      tot = lane < C ? __uint_as_float(sh.x2[lane * kX2 + 0]) : 0.0f;
+    } else {
+      const float m1 = lane < C ? __uint_as_float(sh.x1[lane * kX1 + 0]) : ninf;
+      const float s1 = lane < C ? __uint_as_float(sh.x1[lane * kX1 + 1]) : 0.0f;
+      tot = lane < C ? s1 * __builtin_amdgcn_exp2f((m1 - Mt) * s) / St : 0.0f;
+    }
+    const float mass = resid_mode ? Z : wave_sum(tot);
+    const float thr = it.ug * mass;
+    float before = 0.0f;
+    const int own = (norm_ok && ok2) ? owner_select(tot, C, thr, lane, before) : -1;
+    if (lane == 0) {
+      sh.Z = Z;
+      sh.beta = beta;
+      sh.thr = thr;
+      sh.before = before;
+      sh.owner = own;
+      sh.mode = resid_mode ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  const int owner = sh.owner;
+  const bool t_ok = it.T >= kFltMin && it.T <= kFltMax;
+  int status = (!ok || !ok2) ? 2 : (!t_ok || !norm_ok || !tok_ok) ? 1 : (owner < 0 ? 2 : 0);
+  // the owner chunk decides; a row already known bad is reported by its last chunk
+  const bool decider = (status == 0) ? (it.c == owner) : (it.c == C - 1);
+  if (!decider) return;
   int tok = 0;
   if (status == 0) {
-    const float ug = P.uniforms[t0 + gam];
-    if (!resid_mode) {
-      if (tid < 64) {   // chunk totals of p: s_c 2^((m_c - M) s) / S
-        const bool in = lane < C;
-        const float m1 = in ? __uint_as_float(sh.x1[lane * kX1 + 0]) : ninf;
-        const float s1 = in ? __uint_as_float(sh.x1[lane * kX1 + 1]) : 0.0f;
-        const float pc = in ? s1 * __builtin_amdgcn_exp2f((m1 - Mt) * s) / St : 0.0f;
-        if (in) sh.tot[lane] = pc;
-        const float tz = wave_sum(pc);
-        if (lane == 0) sh.scal[2] = tz;
-      }
-      __syncthreads();
-    }
-    const float thr = ug * (resid_mode ? Z : sh.scal[2]);
-    if (tid < 64) {   // owner chunk
-      float before;
-      const int cs = owner_select(lane < C ? sh.tot[lane] : 0.0f, C, 0.0f, thr, lane, before);
-      if (lane == 0) {
-        sh.scal[3] = before;
-        sh.flag = cs;
-      }
-    }
-    __syncthreads();
-    const int cs = sh.flag;
-    const float Pc = sh.scal[3];
-    if (cs < 0 || cs >= C) {
-      status = 2;   // unreachable for a valid row: the row maximum has weight > 0
-    } else {
-      const float mtc = __uint_as_float(sh.x1[cs * kX1 + 0]);
-      const float mdc = __uint_as_float(sh.x1[cs * kX1 + 2]);
-      const float atc = __builtin_amdgcn_exp2f((mtc - Mt) * s) / St;
-      const float adc = resid_mode ? __builtin_amdgcn_exp2f((mdc - Md) * s) / Sd : 0.0f;
-      const float ctc = chunk_offset(mtc, s);
-      const float cdc = chunk_offset(mdc, s);
-      const int64_t ce0 = (int64_t)cs * kChunk;
-      int ok3 = 1;
-      if (resid_mode) {   // published sub-chunk sums of the owner chunk
-        if (tid < NSUB) {
-          uint32_t v = 0;
-          ok3 = slot_get(P.xch2 + ((int64_t)r * C + cs) * SLOTS2 + kX2Head + tid, tag, spin, v);
-          sh.sub[tid] = __uint_as_float(v);
-        }
-        ok3 = __syncthreads_and(ok3);
-      } else {            // p weights: re-read the owner chunk, sum per sub-chunk
-        float xo[kPerThread];
-        load_chunk<DT>(P.target, r, P.tstride, ce0, P.V, tid, P.t_aligned, xo);
+    // weights in this chunk's own units (the sampled weight of token k is at * w_k)
+    if (sh.mode) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float ws = 0.0f;
-#pragma unroll
-          for (int e = 0; e < EPV; ++e)
-            ws += __builtin_amdgcn_exp2f(__builtin_fmaf(xo[u * EPV + e], s, ctc)) * atc;
-          const float sub = half_sum(ws);
-          if ((tid & (kHalf - 1)) == 0) sh.sub[u * (kThreads / kHalf) + tid / kHalf] = sub;
-        }
-        __syncthreads();
-      }
-      if (!ok3) {
-        status = 2;
-      } else {
-        if (tid < 64) {
-          float before;
-          const int ss = owner_select(lane < NSUB ? sh.sub[lane] : 0.0f, NSUB, Pc, thr, lane, before);
-          int found = -1;
-          if (ss >= 0) {
-            const int su = ss / (kThreads / kHalf);
-            const int sg = ss % (kThreads / kHalf);
-            const int64_t kb = ce0 + (int64_t)su * kThreads * EPV + (int64_t)sg * kHalf * EPV;
-            const int64_t k0 = kb + (int64_t)lane * EPV;
-            float w[EPV];
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-              float wv = 0.0f;
-              if (lane < kHalf && k0 + e < P.V) {
-                const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(
-                    load_one<DT>(P.target, r, P.tstride, k0 + e), s, ctc));
-                if (resid_mode) {
-                  const float ed = __builtin_amdgcn_exp2f(__builtin_fmaf(
-                      load_one<DT>(P.draft, rd, P.dstride, k0 + e), s, cdc));
-                  wv = resid_weight(et, atc, ed, adc);
-                } else {
-                  wv = et * atc;
-                }
-              }
-              w[e] = wv;
-            }
-            const int loc = subchunk_search<EPV>(w, before, thr, lane);
-            if (loc >= 0) found = (int)(kb + loc);
-          }
-          if (lane == 0) sh.flag = found;
-        }
-        __syncthreads();
-        tok = sh.flag;
-        if (tok < 0 || tok >= P.V) status = 2;
-      }
+      for (int k = 0; k < kPerThread; ++k) xt[k] = fmaxf(xt[k] - rho * xd[k], 0.0f);
     }
+    const float tau = (sh.thr - sh.before) / at;
+    const int loc = chunk_search<DT>(xt, tau, sh);
+    tok = it.c * kChunk + loc;
+    if (loc < 0 || tok >= P.V) status = 2;   // unreachable: the owner chunk has weight > 0
   }
   if (tid == 0) {
     bool acc = false;
     if (pair && status == 0) {
-      const float lt = load_one<DT>(P.target, r, P.tstride, xtok);
-      const float ld = load_one<DT>(P.draft, rd, P.dstride, xtok);
-      const float px = __builtin_amdgcn_exp2f(__builtin_fmaf(lt, s, -Mt * s)) / St;
-      const float qx = __builtin_amdgcn_exp2f(__builtin_fmaf(ld, s, -Md * s)) / Sd;
-      acc = P.uniforms[r] * qx < px;
+      const float px = __uint_as_float(sh.x2[C * kX2 + 0]);
+      const float qx = __uint_as_float(sh.x2[C * kX2 + 1]);
+      acc = it.ui * qx < px;
       if (P.p_draft) P.p_draft[rd] = px;
       if (P.q_draft) P.q_draft[rd] = qx;
-      if (P.beta) P.beta[rd] = beta;
-      if (P.resid) P.resid[rd] = Z;
+      if (P.beta) P.beta[rd] = sh.beta;
+      if (P.resid) P.resid[rd] = sh.Z;
     }
-    sh.last = arrive(P, r, b, gam, tag, row_payload(status, acc, tok)) ? 1 : 0;
+    sh.payload = (int)row_payload(status, acc, tok);
   }
   __syncthreads();
-  if (sh.last && tid < 64) resolve(P, b, t0, d0, gam, tag, lane);
+  finish_row(P, it, sh);
 }
 
+// ------------------------------------------------------------------ the kernel
 template <int DT>
 __global__ __launch_bounds__(kThreads) void verify_kernel(Params P) {
+  using F = Fmt<DT>;
   __shared__ Shared sh;
   const int tid = threadIdx.x;
-  const int C = P.C;
-  const int r = (int)(blockIdx.x / (uint32_t)C);   // target row
-  const int c = (int)(blockIdx.x - (uint32_t)r * (uint32_t)C);
+  const int grp = (int)(blockIdx.x % kGroups);
+  if (grp >= P.R_t) return;
+  const int n_items = ((P.R_t - grp + kGroups - 1) / kGroups) * P.C;
+  int idx = (int)(blockIdx.x / kGroups);
+  if (idx >= n_items) return;
 
-  // ---- target row -> (sequence b, position i)
-  int b, gam, d0;
-  if (P.cu_draft == nullptr) {
-    b = r / (P.gamma + 1);
-    gam = P.gamma;
-    d0 = b * P.gamma;
-  } else {
-    int lo = 0, hi = P.B - 1;
-    while (lo < hi) {   // largest b with cu_t[b] = cu_draft[b] + b <= r
-      const int mid = (lo + hi + 1) >> 1;
-      if (P.cu_draft[mid] + mid <= r) lo = mid;
-      else hi = mid - 1;
+  Item it;
+  u32x4 rt[F::U], rdr[F::U];
+  item_place(P, grp, idx, it);
+  issue_chunk<DT>(P.target, it.r, P.tstride, (int64_t)it.c * kChunk, P.V, tid, P.t_aligned, rt);
+  item_lookup(P, it);
+  if (it.pair)
+    issue_chunk<DT>(P.draft, it.d0 + it.i, P.dstride, (int64_t)it.c * kChunk, P.V, tid, P.d_aligned, rdr);
+  while (true) {
+    float xt[kPerThread], xd[kPerThread];
+    unpack<DT>(rt, xt);
+    if (it.pair) unpack<DT>(rdr, xd);
+    // prefetch the next item while this one is processed
+    const int nidx = idx + P.G;
+    const bool more = nidx < n_items;
+    Item nx = it;
+    if (more) {
+      item_place(P, grp, nidx, nx);
+      issue_chunk<DT>(P.target, nx.r, P.tstride, (int64_t)nx.c * kChunk, P.V, tid, P.t_aligned, rt);
+      item_lookup(P, nx);
+      if (nx.pair)
+        issue_chunk<DT>(P.draft, nx.d0 + nx.i, P.dstride, (int64_t)nx.c * kChunk, P.V, tid, P.d_aligned, rdr);
     }
-    b = lo;
-    d0 = P.cu_draft[b];
-    gam = P.cu_draft[b + 1] - d0;
+    if (it.ok) {
+      const bool t_ok = (it.T == 0.0f) || (it.T >= kFltMin && it.T <= kFltMax);
+      __syncthreads();   // shared state of the previous item is no longer read
+      if (t_ok && it.T > 0.0f)
+        sampled_item<DT>(P, it, xt, xd, sh);
+      else
+        greedy_item<DT>(P, it, xt, xd, t_ok, sh);
+    }
+    if (!more) break;
+    idx = nidx;
+    it = nx;
   }
-  const int t0 = d0 + b;   // cu_t[b]
-  const int i = r - t0;
-  if (gam < 0 || d0 < 0 || d0 + gam > P.R_d || i < 0 || i > gam) return;   // inconsistent cu_draft
-  const bool pair = i < gam;
-  const int rd = d0 + i;
-  const float T = P.temps[b];
-  const bool t_ok = (T == 0.0f) || (T >= kFltMin && T <= 3.40282347e38f);
-
-  float xt[kPerThread], xd[kPerThread];
-  const int64_t e0 = (int64_t)c * kChunk;
-  load_chunk<DT>(P.target, r, P.tstride, e0, P.V, tid, P.t_aligned, xt);
-  if (pair) load_chunk<DT>(P.draft, rd, P.dstride, e0, P.V, tid, P.d_aligned, xd);
-  if (t_ok && T > 0.0f)
-    sampled_row<DT>(P, xt, xd, r, c, b, t0, d0, gam, rd, pair, T, sh);
-  else
-    greedy_row<DT>(P, xt, xd, r, c, b, t0, d0, gam, rd, pair, t_ok, sh);
 }
 
 int chunks_for(int V) { return (V + kChunk - 1) / kChunk; }
-int nsub_for(int dtype) { return (kThreads / kHalf) * (dtype == SPECVERIFY_F32 ? Fmt<SPECVERIFY_F32>::U : Fmt<SPECVERIFY_BF16>::U); }
 
 }  // namespace
 
 struct specverify_ctx {
   specverify_config cfg;
   int chunks;
-  int nsub;
   int64_t rows;            // max target rows
+  int cap;                 // workgroups resident at once on the device
   uint64_t* ws;
   size_t ws_bytes;
   uint64_t* xch1;
@@ -877,10 +923,9 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
   h->cfg = *cfg;
   if (h->cfg.spin_limit == 0) h->cfg.spin_limit = kDefaultSpin;
   h->chunks = chunks_for(cfg->vocab);
-  h->nsub = nsub_for(cfg->dtype);
   h->rows = rows;
   const size_t n1 = (size_t)rows * h->chunks * kX1;
-  const size_t n2 = (size_t)rows * h->chunks * (kX2Head + h->nsub);
+  const size_t n2 = (size_t)rows * (h->chunks * kX2 + 2);
   const size_t n3 = (size_t)rows;
   const size_t n4 = (size_t)cfg->max_batch;
   h->ws_bytes = (n1 + n2 + n3 + n4) * sizeof(uint64_t);
@@ -890,8 +935,17 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
     delete h;
     return SPECVERIFY_ERR_DEVICE;
   }
+  // residency of the persistent grid: workgroups per CU times CUs
+  int cus = 0, per_cu = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cfg->device);
+  if (e == hipSuccess)
+    e = cfg->dtype == SPECVERIFY_F32
+            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<SPECVERIFY_F32>, kThreads, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<SPECVERIFY_BF16>, kThreads, 0);
+  h->cap = (e == hipSuccess) ? cus * per_cu : 0;
   void* p = nullptr;
-  hipError_t e = hipMalloc(&p, h->ws_bytes);
+  if (e == hipSuccess && h->cap < kGroups) e = hipErrorInvalidConfiguration;
+  if (e == hipSuccess) e = hipMalloc(&p, h->ws_bytes);
   if (e == hipSuccess) e = hipMemset(p, 0, h->ws_bytes);   // tag 0 is never an epoch
   if (e == hipSuccess) e = hipDeviceSynchronize();
   (void)hipSetDevice(prev);
@@ -938,8 +992,16 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   // Rows that do not start on 16-byte boundaries are read element by element.
   const bool t_aligned = !((uintptr_t)in->target_logits & 15) && !((in->target_stride * esize) & 15);
   const bool d_aligned = R_d > 0 && !((uintptr_t)in->draft_logits & 15) && !((in->draft_stride * esize) & 15);
-  const int64_t blocks = R_t * h->chunks;
-  if (blocks > 0x7FFFFFFF) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+
+  // Persistent grid: per row group, as many workgroups as the device holds
+  // (a whole number of rows' worth when it holds that many), never more
+  // than the group has items.
+  const int C = h->chunks;
+  const int64_t rows_g = (R_t + kGroups - 1) / kGroups;
+  int64_t G = h->cap / kGroups;
+  if (G >= C) G = (G / C) * C;
+  if (G > rows_g * C) G = rows_g * C;
+  if (G < 1) G = 1;
 
   if (++h->epoch == 0) h->epoch = 1;   // 0 never tags a slot (workspace is zeroed)
   Params P;
@@ -954,8 +1016,10 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   P.gamma = in->gamma;
   P.B = B;
   P.R_d = (int32_t)R_d;
+  P.R_t = (int32_t)R_t;
   P.V = V;
-  P.C = h->chunks;
+  P.C = C;
+  P.G = (int32_t)G;
   P.epoch = h->epoch;
   P.spin_limit = h->cfg.spin_limit;
   P.t_aligned = t_aligned;
@@ -975,10 +1039,11 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   (void)hipGetDevice(&prev);
   if (prev != h->cfg.device && hipSetDevice(h->cfg.device) != hipSuccess) return SPECVERIFY_ERR_DEVICE;
   hipStream_t stream = (hipStream_t)hip_stream;
+  const dim3 grid((uint32_t)(G * kGroups));
   if (h->cfg.dtype == SPECVERIFY_F32)
-    hipLaunchKernelGGL(verify_kernel<SPECVERIFY_F32>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, P);
+    hipLaunchKernelGGL(verify_kernel<SPECVERIFY_F32>, grid, dim3(kThreads), 0, stream, P);
   else
-    hipLaunchKernelGGL(verify_kernel<SPECVERIFY_BF16>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, P);
+    hipLaunchKernelGGL(verify_kernel<SPECVERIFY_BF16>, grid, dim3(kThreads), 0, stream, P);
   const hipError_t e = hipGetLastError();
   if (prev != h->cfg.device) (void)hipSetDevice(prev);
   return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_ERR_DEVICE;
