@@ -24,6 +24,9 @@
  * cu_draft[b+1] - 1 and target rows cu_t[b] .. cu_t[b] + gamma_b with
  * cu_t[b] = cu_draft[b] + b (so R_t = R_d + B target rows in total).
  * A uniform draft length is the special case cu_draft[b] = b * gamma.
+ * cu_draft must be non-decreasing with cu_draft[0] = 0 and cu_draft[B] =
+ * R_d; a sequence whose own entries break this reports accepted_len -1, and
+ * no memory outside the declared buffers is touched for any cu_draft.
  *
  * Ownership.  The caller owns every input and output buffer (device
  * memory).  A handle owns only its device workspace, allocated in
@@ -67,7 +70,7 @@ typedef enum {
 typedef enum { SPECVERIFY_F32 = 0, SPECVERIFY_BF16 = 1 } specverify_dtype;
 
 /* Fixed per handle.  Limits: 1 <= vocab <= 524288 (64 chunks of 8192),
- * max_batch >= 1, max_gamma >= 0, max_batch * (max_gamma + 1) <= 2^24. */
+ * max_batch >= 1, 0 <= max_gamma <= 255, max_batch * (max_gamma + 1) <= 2^24. */
 typedef struct {
   int32_t max_batch;   /* largest B a run may use                                 */
   int32_t max_gamma;   /* largest draft length; bounds R_t <= max_batch*(max_gamma+1) */
@@ -124,6 +127,14 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
 
 /* Free the workspace and the handle (NULL is accepted). */
 specverify_status specverify_destroy(specverify_handle h);
+
+/* Timing of the two kernels a run launches (the streaming pass over the
+ * logits, then the per-sequence finish), measured with HIP events on the
+ * run's stream.  set_timing(h, 1) makes every later run record the events;
+ * last_timing waits for the last run and returns both durations in
+ * milliseconds (INVALID_ARGUMENT if timing is off or a pointer is NULL). */
+specverify_status specverify_set_timing(specverify_handle h, int32_t enable);
+specverify_status specverify_last_timing(specverify_handle h, float* stream_ms, float* finish_ms);
 
 /* Number of V-chunks (8192 logits each) a row is split into for this
  * handle, and the workspace size in bytes; for tools and tests. */

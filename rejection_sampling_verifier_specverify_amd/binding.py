@@ -21,6 +21,7 @@ F32, BF16 = 0, 1
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "DEVICE"}
 CHUNK = 8192          # logits per V-chunk (one workgroup)
 EXPORTED = ("specverify_create", "specverify_run", "specverify_destroy",
+            "specverify_set_timing", "specverify_last_timing",
             "specverify_chunks_per_row", "specverify_workspace_bytes")
 
 
@@ -82,6 +83,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.specverify_chunks_per_row.restype = ctypes.c_int32
     lib.specverify_workspace_bytes.argtypes = [ctypes.c_void_p]
     lib.specverify_workspace_bytes.restype = ctypes.c_int64
+    lib.specverify_set_timing.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    lib.specverify_set_timing.restype = ctypes.c_int
+    lib.specverify_last_timing.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float),
+                                           ctypes.POINTER(ctypes.c_float)]
+    lib.specverify_last_timing.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -129,6 +135,19 @@ class SpecVerify:
         lib = load_library()
         self.chunks = int(lib.specverify_chunks_per_row(self.handle))
         self.workspace_bytes = int(lib.specverify_workspace_bytes(self.handle))
+
+    def set_timing(self, enable: bool) -> None:
+        st = load_library().specverify_set_timing(self.handle, 1 if enable else 0)
+        if st != OK:
+            raise SpecVerifyError("specverify_set_timing", st)
+
+    def last_timing(self):
+        """(stream_ms, finish_ms) of the last run; waits for it."""
+        a, f = ctypes.c_float(), ctypes.c_float()
+        st = load_library().specverify_last_timing(self.handle, ctypes.byref(a), ctypes.byref(f))
+        if st != OK:
+            raise SpecVerifyError("specverify_last_timing", st)
+        return a.value, f.value
 
     def close(self) -> None:
         if getattr(self, "handle", None):
