@@ -11,12 +11,26 @@ rotates over enough copies of the batch (> 2x the 256 MB Infinity Cache)
 that no step reads logits the previous steps left in the cache.  HIP events
 on the launch stream bracket the K timed steps.  Prints one JSON line.
 
+Kernel durations come from HIP events that the library records on the same
+stream around each of its two launches, over a repeat of the K steps (kept
+out of the timed region because events between kernels add gaps); the HBM bytes
+the streaming kernel actually moves come from a rocprofv3 counter summary
+(FETCH_SIZE and WRITE_SIZE, scaled by what the same counters read for a plain
+copy of known size), reported only while the kernel source still hashes to
+the one that summary was taken from.
+
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
                   [--no-cpu-baseline] [--copy-probe]
+  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --out FILE --command-fetch CMD
+                  --command-write CMD      (writes the traffic summary from two
+                                            rocprofv3 --pmc output folders)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +44,17 @@ sys.path.insert(0, ROOT)
 METRIC = "verified rows/s + logits GB/s (frac of HBM peak), B=64 γ=4 V=128256 bf16"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
 MALL_BYTES = 256 << 20          # Infinity Cache
+KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verifier_specverify_amd", "csrc", "specverify.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"stream_kernel_{workload}_hbm_traffic.txt")
+
+
+def source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def parse():
@@ -43,32 +68,128 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of the logits' size (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--out")
+    ap.add_argument("--command-fetch", default="")
+    ap.add_argument("--command-write", default="")
     return ap.parse_args()
 
 
+def _pmc_rows(folder: str, counter: str):
+    """(dispatch id, kernel name, value) of one counter from a rocprofv3 --pmc csv output."""
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    out = []
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return sorted(out)
+
+
+def summarize_pmc(args):
+    """HBM traffic per launch of stream_kernel: FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch) averaged over its dispatches, each scaled by bytes / counter
+    of the copy probe (the plain copies dispatched after the last verifier
+    launch, of exactly the logits' size)."""
+    from rejection_sampling_verifier_specverify_amd.workloads import WORKLOADS, make_inputs
+    w = WORKLOADS[args.workload]
+    copy_bytes = logit_bytes_of(w)
+    res = {}
+    for name, folder in (("FETCH_SIZE", args.summarize_pmc[0]), ("WRITE_SIZE", args.summarize_pmc[1])):
+        rows = _pmc_rows(folder, name)
+        ker = [(d, v) for d, k, v in rows if "stream_kernel" in k]
+        if not ker:
+            raise SystemExit(f"{name}: no stream_kernel dispatch in {folder}")
+        last = max(d for d, _ in ker)
+        cp = [v for d, k, v in rows if d > last and "copy" in k.lower()]
+        if not cp:
+            raise SystemExit(f"{name}: no copy-probe dispatch after the last stream_kernel in {folder}")
+        kv = float(np.mean([v for _, v in ker]))
+        cv = float(np.mean(cp))
+        res[name] = dict(kernel_kib=kv, copy_kib=cv, factor=copy_bytes / (cv * 1024.0),
+                         n_kernel=len(ker), n_copy=len(cp))
+    fetch = res["FETCH_SIZE"]["kernel_kib"] * 1024.0 * res["FETCH_SIZE"]["factor"]
+    write = res["WRITE_SIZE"]["kernel_kib"] * 1024.0 * res["WRITE_SIZE"]["factor"]
+    lines = [
+        f"# HBM traffic of stream_kernel, workload {w.name}",
+        "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by",
+        "# copy_bytes / (1024 * what the counter reads for a plain copy of copy_bytes).",
+        f"command_fetch: {args.command_fetch}",
+        f"command_write: {args.command_write}",
+        f"source_sha256: {source_hash()}",
+        f"copy_bytes: {copy_bytes}",
+    ]
+    for name, r in res.items():
+        lines += [f"{name.lower()}_kernel_kib_per_dispatch: {r['kernel_kib']:.1f}",
+                  f"{name.lower()}_kernel_dispatches: {r['n_kernel']}",
+                  f"{name.lower()}_copy_kib_per_dispatch: {r['copy_kib']:.1f}",
+                  f"{name.lower()}_copy_dispatches: {r['n_copy']}",
+                  f"{name.lower()}_factor: {r['factor']:.5f}"]
+    lines += [f"fetch_bytes_per_launch: {fetch:.0f}",
+              f"write_bytes_per_launch: {write:.0f}",
+              f"traffic_bytes_per_launch: {fetch + write:.0f}",
+              f"algorithmic_logit_bytes_per_launch: {logit_bytes_of(w)}"]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def logit_bytes_of(w) -> int:
+    """Every logit of the workload once: sum over sequences of (2 gamma + 1) rows of V."""
+    from rejection_sampling_verifier_specverify_amd.workloads import make_inputs
+    return int(make_inputs(w, seed=0).logit_bytes)
+
+
+def read_traffic(workload: str):
+    """Traffic bytes per launch from the committed summary, or None when there
+    is none or it was taken from another version of the kernel source."""
+    fn = traffic_file(workload)
+    if not os.path.exists(fn):
+        return None
+    kv = {}
+    with open(fn) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(inp, budget_s: float):
-    """Time the float64 oracle on the host over whole sequences until the budget
-    is spent (at least one sequence); one process."""
+    """Time the float64 oracle on the host, one sequence per call, cycling over
+    the benchmarked batch until the budget is spent; one process, one thread."""
     from oracle import verify_batch
     B = inp.batch
     rows = 0
+    seqs = 0
     t0 = time.perf_counter()
-    done = 0
-    for b in range(B):
+    while True:
+        b = seqs % B
         verify_batch(inp.target, inp.draft, inp.draft_tokens, inp.uniforms, inp.temperatures,
                      inp.cu_draft, inp.workload.dtype, sequences=[b])
         rows += int(inp.gammas[b]) + 1
-        done += 1
+        seqs += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     return dict(value=rows / dt, unit="rows/s", cores=1, kind="oracle",
-                sample=f"first {done} of {B} sequences of the benchmarked batch ({rows} target rows), "
-                       f"float64 numpy, one process, {dt:.1f} s")
+                sample=f"{seqs} sequence verifications cycling over the {B} sequences of the "
+                       f"benchmarked batch ({rows} target rows, {dt:.1f} s), float64 numpy, "
+                       f"one process, one thread")
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        if not args.out:
+            raise SystemExit("--summarize-pmc needs --out")
+        summarize_pmc(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the verifier "
               "shards over sequences with no communication, so N GPUs run N independent copies "
@@ -114,29 +235,28 @@ def main():
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
-    # per-step events give the spread; the outer pair gives the mean
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # Timed region: K steps between two events on torch's current stream, which
+    # is the launch stream; nothing else is recorded in between.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    evs[0].record(stream)
+    ev0.record(stream)
     for k in range(args.steps):
         step(k)
-        evs[k + 1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
-    total_ms = evs[0].elapsed_time(evs[-1])
-    per = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps)])
-    ms = total_ms / args.steps
+    ms = ev0.elapsed_time(ev1) / args.steps
 
-    # per-kernel durations (HIP events around each of the two kernels)
+    # Kernel durations: the same K steps again, with the library recording HIP
+    # events around each of its two launches on the launch stream.  The events
+    # between the kernels add dispatch gaps, so this pass is kept out of the
+    # timed region above.
     sv.set_timing(True)
-    ks, kf = [], []
-    for k in range(min(args.steps, 100)):
+    for k in range(args.steps):
         step(k)
-        a, f = sv.last_timing()
-        ks.append(a)
-        kf.append(f)
+    nrec, ks, kf = sv.timing_totals()
     sv.set_timing(False)
-    stream_ms = float(np.mean(ks))
-    finish_ms = float(np.mean(kf))
+    stream_ms = ks / nrec
+    finish_ms = kf / nrec
 
     if args.copy_probe:   # plain copy of the logits' size, for FETCH/WRITE_SIZE calibration
         src = torch.empty(logit_bytes // 2, dtype=torch.int16, device=dev)
@@ -150,6 +270,7 @@ def main():
     small_out = 4 * B + 4 * R_t + 16 * R_d
     alg_bytes = logit_bytes + small_in + small_out
     gbps = logit_bytes / (stream_ms * 1e-3) / 1e9
+    traffic = read_traffic(w.name)
     res = {
         "metric": METRIC,
         "value": R_t / (ms * 1e-3),
@@ -168,11 +289,10 @@ def main():
                    "rotating_copies": ncopy, "seed": args.seed},
         "logits_GBps": logit_bytes / (ms * 1e-3) / 1e9,
         "sequences_per_s": B / (ms * 1e-3),
-        "step_us_p10_p50_p90": [float(np.percentile(per, q) * 1e3) for q in (10, 50, 90)],
         "kernel_ms": {"stream": stream_ms, "finish": finish_ms},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "stream_kernel",
-                     "alg_bytes_per_launch": logit_bytes},
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic, "kernel": "stream_kernel",
+                     "alg_bytes_per_launch": logit_bytes, "kernel_launches_timed": nrec},
         "step_GBps": alg_bytes / (ms * 1e-3) / 1e9,
     }
     if not args.no_cpu_baseline:

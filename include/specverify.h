@@ -129,12 +129,18 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
 specverify_status specverify_destroy(specverify_handle h);
 
 /* Timing of the two kernels a run launches (the streaming pass over the
- * logits, then the per-sequence finish), measured with HIP events on the
- * run's stream.  set_timing(h, 1) makes every later run record the events;
- * last_timing waits for the last run and returns both durations in
- * milliseconds (INVALID_ARGUMENT if timing is off or a pointer is NULL). */
+ * logits, then the per-sequence finish), measured with HIP events recorded on
+ * the run's stream around each launch.  set_timing(h, 1) starts a new
+ * measurement: the next SPECVERIFY_TIMING_RUNS runs record their events (later
+ * runs record none); set_timing(h, 0) stops recording.  timing_totals waits
+ * for the last recorded run and returns the number of recorded runs and the
+ * summed durations of both kernels in milliseconds, then starts counting
+ * afresh.  Errors: INVALID_ARGUMENT for a NULL pointer, DEVICE if an event
+ * call fails (also from set_timing, which creates the events). */
+#define SPECVERIFY_TIMING_RUNS 1024
 specverify_status specverify_set_timing(specverify_handle h, int32_t enable);
-specverify_status specverify_last_timing(specverify_handle h, float* stream_ms, float* finish_ms);
+specverify_status specverify_timing_totals(specverify_handle h, int32_t* runs, float* stream_ms,
+                                           float* finish_ms);
 
 /* Number of V-chunks (8192 logits each) a row is split into for this
  * handle, and the workspace size in bytes; for tools and tests. */

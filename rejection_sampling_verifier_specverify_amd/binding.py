@@ -21,7 +21,7 @@ F32, BF16 = 0, 1
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "DEVICE"}
 CHUNK = 8192          # logits per V-chunk (one workgroup)
 EXPORTED = ("specverify_create", "specverify_run", "specverify_destroy",
-            "specverify_set_timing", "specverify_last_timing",
+            "specverify_set_timing", "specverify_timing_totals",
             "specverify_chunks_per_row", "specverify_workspace_bytes")
 
 
@@ -85,9 +85,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.specverify_workspace_bytes.restype = ctypes.c_int64
     lib.specverify_set_timing.argtypes = [ctypes.c_void_p, ctypes.c_int32]
     lib.specverify_set_timing.restype = ctypes.c_int
-    lib.specverify_last_timing.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float),
-                                           ctypes.POINTER(ctypes.c_float)]
-    lib.specverify_last_timing.restype = ctypes.c_int
+    lib.specverify_timing_totals.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32),
+                                             ctypes.POINTER(ctypes.c_float),
+                                             ctypes.POINTER(ctypes.c_float)]
+    lib.specverify_timing_totals.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -141,13 +142,15 @@ class SpecVerify:
         if st != OK:
             raise SpecVerifyError("specverify_set_timing", st)
 
-    def last_timing(self):
-        """(stream_ms, finish_ms) of the last run; waits for it."""
-        a, f = ctypes.c_float(), ctypes.c_float()
-        st = load_library().specverify_last_timing(self.handle, ctypes.byref(a), ctypes.byref(f))
+    def timing_totals(self):
+        """(runs, stream_ms, finish_ms): the runs recorded since timing was
+        enabled (or last read) and the summed kernel durations; waits for them."""
+        n, a, f = ctypes.c_int32(), ctypes.c_float(), ctypes.c_float()
+        st = load_library().specverify_timing_totals(self.handle, ctypes.byref(n), ctypes.byref(a),
+                                                     ctypes.byref(f))
         if st != OK:
-            raise SpecVerifyError("specverify_last_timing", st)
-        return a.value, f.value
+            raise SpecVerifyError("specverify_timing_totals", st)
+        return n.value, a.value, f.value
 
     def close(self) -> None:
         if getattr(self, "handle", None):

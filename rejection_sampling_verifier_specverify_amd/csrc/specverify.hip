@@ -967,8 +967,9 @@ struct specverify_ctx {
   float* part;
   float* rowpart;
   uint32_t epoch;
-  int timing;
-  hipEvent_t ev[3];
+  int timing;              // recording events
+  int trec;                // runs recorded since the measurement started
+  hipEvent_t* ev;          // [SPECVERIFY_TIMING_RUNS][3], created on first use
 };
 
 extern "C" {
@@ -1010,15 +1011,12 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_kernel<SPECVERIFY_BF16>, kThreads, 0);
   h->cap = (e == hipSuccess) ? cus * per_cu : 0;
   void* p = nullptr;
-  int nev = 0;
   if (e == hipSuccess && h->cap < kGroups) e = hipErrorInvalidConfiguration;
   if (e == hipSuccess) e = hipMalloc(&p, h->ws_bytes);
   if (e == hipSuccess) e = hipMemset(p, 0, h->ws_bytes);   // tag 0 is never an epoch
-  for (; e == hipSuccess && nev < 3; ++nev) e = hipEventCreate(&h->ev[nev]);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   (void)hipSetDevice(prev);
   if (e != hipSuccess) {
-    for (int k = 0; k < nev; ++k) (void)hipEventDestroy(h->ev[k]);
     if (p) (void)hipFree(p);
     delete h;
     return e == hipErrorOutOfMemory ? SPECVERIFY_ERR_OUT_OF_MEMORY : SPECVERIFY_ERR_DEVICE;
@@ -1029,6 +1027,8 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
   h->rowpart = (float*)((char*)p + n1 + n2);
   h->epoch = 0;
   h->timing = 0;
+  h->trec = 0;
+  h->ev = nullptr;
   *out = h;
   return SPECVERIFY_OK;
 }
@@ -1112,17 +1112,19 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   hipStream_t stream = (hipStream_t)hip_stream;
   const dim3 grid((uint32_t)(G * kGroups));
   hipError_t e = hipSuccess;
-  if (h->timing) e = hipEventRecord(h->ev[0], stream);
+  hipEvent_t* ev = nullptr;
+  if (h->timing && h->trec < SPECVERIFY_TIMING_RUNS) ev = h->ev + 3 * h->trec++;
+  if (ev) e = hipEventRecord(ev[0], stream);
   if (h->cfg.dtype == SPECVERIFY_F32) {
     hipLaunchKernelGGL(stream_kernel<SPECVERIFY_F32>, grid, dim3(kThreads), 0, stream, P);
-    if (h->timing && e == hipSuccess) e = hipEventRecord(h->ev[1], stream);
+    if (ev && e == hipSuccess) e = hipEventRecord(ev[1], stream);
     hipLaunchKernelGGL(finish_kernel<SPECVERIFY_F32>, dim3(B), dim3(64 * fwaves), 0, stream, P);
   } else {
     hipLaunchKernelGGL(stream_kernel<SPECVERIFY_BF16>, grid, dim3(kThreads), 0, stream, P);
-    if (h->timing && e == hipSuccess) e = hipEventRecord(h->ev[1], stream);
+    if (ev && e == hipSuccess) e = hipEventRecord(ev[1], stream);
     hipLaunchKernelGGL(finish_kernel<SPECVERIFY_BF16>, dim3(B), dim3(64 * fwaves), 0, stream, P);
   }
-  if (h->timing && e == hipSuccess) e = hipEventRecord(h->ev[2], stream);
+  if (ev && e == hipSuccess) e = hipEventRecord(ev[2], stream);
   const hipError_t e2 = hipGetLastError();
   if (prev != h->cfg.device) (void)hipSetDevice(prev);
   return (e == hipSuccess && e2 == hipSuccess) ? SPECVERIFY_OK : SPECVERIFY_ERR_DEVICE;
@@ -1133,7 +1135,9 @@ specverify_status specverify_destroy(specverify_handle h) {
   int prev = 0;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(h->cfg.device);
-  for (int k = 0; k < 3; ++k) (void)hipEventDestroy(h->ev[k]);
+  if (h->ev)
+    for (int k = 0; k < 3 * SPECVERIFY_TIMING_RUNS; ++k) (void)hipEventDestroy(h->ev[k]);
+  delete[] h->ev;
   (void)hipFree(h->ws);
   (void)hipSetDevice(prev);
   delete h;
@@ -1142,16 +1146,49 @@ specverify_status specverify_destroy(specverify_handle h) {
 
 specverify_status specverify_set_timing(specverify_handle h, int32_t enable) {
   if (!h) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  if (enable && !h->ev) {
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECVERIFY_ERR_DEVICE;
+    hipEvent_t* ev = new (std::nothrow) hipEvent_t[3 * SPECVERIFY_TIMING_RUNS];
+    int n = 0;
+    hipError_t e = ev ? hipSuccess : hipErrorOutOfMemory;
+    for (; e == hipSuccess && n < 3 * SPECVERIFY_TIMING_RUNS; ++n) e = hipEventCreate(&ev[n]);
+    (void)hipSetDevice(prev);
+    if (e != hipSuccess) {
+      for (int k = 0; k < n - 1; ++k) (void)hipEventDestroy(ev[k]);
+      delete[] ev;
+      return SPECVERIFY_ERR_DEVICE;
+    }
+    h->ev = ev;
+  }
   h->timing = enable ? 1 : 0;
+  if (enable) h->trec = 0;
   return SPECVERIFY_OK;
 }
 
-specverify_status specverify_last_timing(specverify_handle h, float* stream_ms, float* finish_ms) {
-  if (!h || !stream_ms || !finish_ms || !h->timing) return SPECVERIFY_ERR_INVALID_ARGUMENT;
-  if (hipEventSynchronize(h->ev[2]) != hipSuccess) return SPECVERIFY_ERR_DEVICE;
-  if (hipEventElapsedTime(stream_ms, h->ev[0], h->ev[1]) != hipSuccess ||
-      hipEventElapsedTime(finish_ms, h->ev[1], h->ev[2]) != hipSuccess)
-    return SPECVERIFY_ERR_DEVICE;
+specverify_status specverify_timing_totals(specverify_handle h, int32_t* runs, float* stream_ms,
+                                           float* finish_ms) {
+  if (!h || !runs || !stream_ms || !finish_ms) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  *runs = 0;
+  *stream_ms = 0.0f;
+  *finish_ms = 0.0f;
+  if (h->trec == 0) return SPECVERIFY_OK;
+  const hipEvent_t* ev = h->ev;
+  if (hipEventSynchronize(ev[3 * (h->trec - 1) + 2]) != hipSuccess) return SPECVERIFY_ERR_DEVICE;
+  double a = 0.0, f = 0.0;
+  for (int k = 0; k < h->trec; ++k) {
+    float x = 0.0f, y = 0.0f;
+    if (hipEventElapsedTime(&x, ev[3 * k], ev[3 * k + 1]) != hipSuccess ||
+        hipEventElapsedTime(&y, ev[3 * k + 1], ev[3 * k + 2]) != hipSuccess)
+      return SPECVERIFY_ERR_DEVICE;
+    a += x;
+    f += y;
+  }
+  *runs = h->trec;
+  *stream_ms = (float)a;
+  *finish_ms = (float)f;
+  h->trec = 0;
   return SPECVERIFY_OK;
 }
 
