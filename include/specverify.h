@@ -24,9 +24,10 @@
  * cu_draft[b+1] - 1 and target rows cu_t[b] .. cu_t[b] + gamma_b with
  * cu_t[b] = cu_draft[b] + b (so R_t = R_d + B target rows in total).
  * A uniform draft length is the special case cu_draft[b] = b * gamma.
- * cu_draft must be non-decreasing with cu_draft[0] = 0 and cu_draft[B] =
- * R_d; a sequence whose own entries break this reports accepted_len -1, and
- * no memory outside the declared buffers is touched for any cu_draft.
+ * cu_draft must be non-decreasing with cu_draft[0] = 0, cu_draft[B] = R_d
+ * and every gamma_b <= max_gamma; if it is not, every sequence reports
+ * accepted_len -1 and every out_tokens entry is -1, and no memory outside
+ * the declared buffers is touched for any cu_draft.
  *
  * Ownership.  The caller owns every input and output buffer (device
  * memory).  A handle owns only its device workspace, allocated in
@@ -44,9 +45,10 @@
  * reported in accepted_len: -1 = invalid data (a NaN or +inf logit in any
  * of the sequence's rows, a row of only -inf, a drafted token outside
  * [0, V), a temperature that is negative, not finite or in (0, FLT_MIN)),
- * -2 = a bounded wait inside the kernel expired (never in normal
- * operation; the kernel always terminates).  The tokens of such a
- * sequence are -1 and its diagnostics unspecified.
+ * -2 = internal error: statistics of one of the sequence's rows were
+ * missing when the sequence was resolved (not expected to happen; the
+ * kernels always terminate).  The tokens of such a sequence are -1 and its
+ * diagnostics unspecified.
  */
 #ifndef SPECVERIFY_H_
 #define SPECVERIFY_H_
@@ -69,15 +71,20 @@ typedef enum {
 
 typedef enum { SPECVERIFY_F32 = 0, SPECVERIFY_BF16 = 1 } specverify_dtype;
 
-/* Fixed per handle.  Limits: 1 <= vocab <= 524288 (64 chunks of 8192),
- * max_batch >= 1, 0 <= max_gamma <= 255, max_batch * (max_gamma + 1) <= 2^24. */
+/* Fixed per handle.  Limits: 1 <= vocab <= 262144 (at most 128 chunks of
+ * 4 KB per bf16 row, 256 per f32 row), max_batch >= 1,
+ * 0 <= max_gamma <= 255, max_batch * (max_gamma + 1) <= 2^24.  create also
+ * returns UNSUPPORTED on a device too small to keep one row's chunks in
+ * flight together (fewer than 8 * chunks resident waves). */
 typedef struct {
   int32_t max_batch;   /* largest B a run may use                                 */
   int32_t max_gamma;   /* largest draft length; bounds R_t <= max_batch*(max_gamma+1) */
   int32_t vocab;       /* V of every logits row                                   */
   int32_t dtype;       /* specverify_dtype of both logits tensors                 */
   int32_t device;      /* HIP device ordinal the workspace lives on               */
-  int32_t spin_limit;  /* polls before a wait gives up (0 = default, ~seconds)    */
+  int32_t spin_limit;  /* polls for other waves' chunk statistics before a wave
+                          computes the missing ones itself (0 = default, 64; at
+                          most 2^20); any value gives the same results             */
 } specverify_config;
 
 /* Inputs of one run; every pointer is device memory. */
@@ -86,8 +93,10 @@ typedef struct {
   int32_t gamma;              /* uniform draft length, used iff cu_draft == NULL   */
   const int32_t* cu_draft;    /* [B+1] prefix offsets of draft rows, or NULL       */
   int32_t num_draft_rows;     /* R_d = cu_draft[B] (host copy), used iff cu_draft  */
-  const void* target_logits;  /* [R_t, target_stride] f32 or bf16; rows that start on
-                                 16-byte boundaries take the vector-load path       */
+  const void* target_logits;  /* [R_t, target_stride] f32 or bf16; when both tensors'
+                                 rows start on 16-byte boundaries and V * esize is a
+                                 multiple of 16 the kernels use 16-byte loads, else
+                                 element loads                                      */
   int64_t target_stride;      /* elements between rows, >= V                       */
   const void* draft_logits;   /* [R_d, draft_stride]; may be NULL iff R_d == 0     */
   int64_t draft_stride;
@@ -128,9 +137,9 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
 /* Free the workspace and the handle (NULL is accepted). */
 specverify_status specverify_destroy(specverify_handle h);
 
-/* Timing of the two kernels a run launches (the streaming pass over the
- * logits, then the per-sequence finish), measured with HIP events recorded on
- * the run's stream around each launch.  set_timing(h, 1) starts a new
+/* Timing of a run's kernels, measured with HIP events recorded on the run's
+ * stream: stream_ms covers the layout check (ragged batches only) and the
+ * streaming pass over the logits, finish_ms the per-sequence finish.  set_timing(h, 1) starts a new
  * measurement: the next SPECVERIFY_TIMING_RUNS runs record their events (later
  * runs record none); set_timing(h, 0) stops recording.  timing_totals waits
  * for the last recorded run and returns the number of recorded runs and the
@@ -142,8 +151,9 @@ specverify_status specverify_set_timing(specverify_handle h, int32_t enable);
 specverify_status specverify_timing_totals(specverify_handle h, int32_t* runs, float* stream_ms,
                                            float* finish_ms);
 
-/* Number of V-chunks (8192 logits each) a row is split into for this
- * handle, and the workspace size in bytes; for tools and tests. */
+/* Number of V-chunks (4 KB of a row: 2048 bf16 or 1024 f32 logits) a row
+ * is split into for this handle, and the workspace size in bytes; for tools
+ * and tests. */
 int32_t specverify_chunks_per_row(specverify_handle h);
 int64_t specverify_workspace_bytes(specverify_handle h);
 

@@ -14,12 +14,14 @@ import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libspecverify.so")
+# SPECVERIFY_LIB selects another build of the library (same ABI)
+LIB_PATH = os.environ.get("SPECVERIFY_LIB", os.path.join(PKG, "libspecverify.so"))
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_OUT_OF_MEMORY, ERR_DEVICE = range(5)
 F32, BF16 = 0, 1
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "DEVICE"}
-CHUNK = 8192          # logits per V-chunk (one workgroup)
+CHUNK = {"bf16": 2048, "f32": 1024}   # logits per V-chunk (4 KB of a row: one wave's item)
+MAX_CHUNKS = {"bf16": 128, "f32": 256}
 EXPORTED = ("specverify_create", "specverify_run", "specverify_destroy",
             "specverify_set_timing", "specverify_timing_totals",
             "specverify_chunks_per_row", "specverify_workspace_bytes")

@@ -7,45 +7,57 @@
 // Scale Your Model -- All About Transformer Inference", Appendix D): see
 // include/specverify.h.
 //
-// Two kernels run back to back on the caller's stream.
+// A run launches up to three kernels on the caller's stream.
 //
-// stream_kernel reads every logit from HBM exactly once.  Target rows are
-// split into chunks of 8192 logits; a work item is one chunk of one target
-// row plus, when the position has a draft, the same chunk of the draft row,
-// so p_k and q_k of the same token meet in the same registers.  The kernel
-// is persistent: as many 256-thread workgroups as the GPU holds at once.
-// Rows are dealt round robin to eight groups that match the eight XCDs
-// (workgroup b runs on XCD b % 8); inside a group, workgroup j takes items
-// j, j + G, j + 2G, ... of the group's row-major item list, so the chunks of
-// a row run together, in one round, on one XCD, and the 16-byte loads of a
-// workgroup's next item are in flight while it works on the current one.
-//   phase 1   chunk max m_c; e_k = 2^(l_k s - m_c s), s = log2(e) / T, kept
-//             in registers; chunk sum s_c and sums over 32-lane sub-chunks.
-//             T = 0: chunk argmax.
-//   xch 1     (m_c, s_c) of target and draft go into epoch-tagged slots.
-//             Rows with a draft read all of their row's slots and merge
-//             them, (max, sum 2^((m_c - M) s)): the row normalisers M, S.
-//   phase 2   with a_c = 2^((m_c - M) s) / S for target (t) and draft (d) and
-//             rho = a_d / a_t: p_k = a_t e_t and q_k = a_t rho e_d, so
+// layout_kernel (ragged batches only) checks cu_draft and writes one
+// record per target row: sequence, draft row, whether the position has a
+// draft, temperature.
+//
+// stream_kernel reads every logit from HBM exactly once.  Its unit of work
+// is an item: 4 KB of one target row (a chunk of 2048 bf16 or 1024 fp32
+// logits) plus the same chunk of the draft row when the position has one,
+// so p_k and q_k of a token meet in the same lane.  One wave owns one item
+// at a time; the four waves of a workgroup are independent (no barriers,
+// no LDS).  The grid is persistent (what the GPU holds at once).  Rows are
+// dealt round robin to eight groups matching the eight XCDs (workgroup b
+// runs on XCD b % 8); wave j of a group takes items j, j + Gw, j + 2 Gw, ...
+// of the group's row-major item list, so the chunks of a row are handled in
+// one round by waves of one XCD.
+//   phase 1   chunk max m_c (DPP), e_k = 2^(l_k s - m_c s) with s = log2(e)/T
+//             kept in registers, chunk sum s_c; (m_c, s_c) of target and
+//             draft go out in epoch-tagged slots.  T = 0: chunk argmax.
+//   phase 2   once every chunk of the row has published: the row normalisers
+//             (M, S) = merge of (m_c, s_c); with a_c = 2^((m_c - M) s) / S and
+//             rho = a_d / a_t, p_k = a_t e_t and q_k = a_t rho e_d, so
 //             min(p, q) = a_t min(e_t, rho e_d) and max(0, p - q) =
-//             a_t max(0, e_t - rho e_d).  Chunk sums of both (beta, velog
-//             section 2-3 item 1; residual mass Z, item 2) and sub-chunk sums
-//             of the residual go out; the chunk holding the drafted token
-//             writes p(x) and q(x).
+//             a_t (e_t - min(e_t, rho e_d)); the chunk sums of both (beta,
+//             velog section 2-3 item 1; residual mass Z, item 2) go out.
+// The waves are software pipelined: while the slots of item k's row are in
+// flight, the wave runs phase 1 of item k + 1, and the 16-byte loads of
+// item k + 2 are in flight behind both.  The poll of item k's slots is
+// issued before the loads of item k + 2, so waiting for it never waits for
+// them.  Logits are read with buffer loads: a row without a draft gets a
+// zero-sized buffer, so every item issues the same loads and none of them
+// touches memory it should not.
+//
 // finish_kernel, one workgroup per sequence and one wave per row, then
-// merges the partials: Z and beta; the chunk, then the 32-lane sub-chunk,
-// whose CDF interval holds u_gamma * Z (or the CDF of p for the bonus row and
-// when Z = 0); the 256 (bf16) or 128 (fp32) logits of that sub-chunk are
-// re-read and scanned for the token; the acceptance test u_i q(x) < p(x);
+// merges the partials: Z and beta; p(x) and q(x) from the two logits of the
+// drafted token; the chunk whose CDF interval holds u_gamma * Z (or the CDF
+// of p for the bonus row and when Z = 0), whose logits it re-reads and scans
+// in token order for the token; the acceptance test u_i q(x) < p(x);
 // finally the sequence's first rejection n, accepted_len and the n + 1
 // tokens.  The accepted length never leaves the device.
 //
-// Inside stream_kernel, values cross workgroups only in 64-bit slots that
-// carry a 32-bit epoch tag next to the value, written and read with
-// agent-scope atomics, so a reader that sees the tag sees the value; no
-// fences.  Every wait is bounded; an expired wait is reported as
-// accepted_len = -2 and the kernels still end.  finish_kernel reads what
-// stream_kernel wrote after the kernel boundary.
+// Inside stream_kernel, values cross waves only in 64-bit slots that carry a
+// 32-bit epoch tag next to the value.  A slot is written with one aligned
+// 64-bit store (the CU's L1 writes through to the XCD's L2) and polled with
+// loads that skip L1 and read that L2; the waves that meet over a row all run
+// on one XCD, so a reader that sees the tag sees the value, without fences or
+// atomics.  Nothing guarantees that every workgroup of the grid is resident
+// at once, so a wave that has polled spin_limit times reads the chunks that
+// are still missing and computes their statistics itself (bit-identical to
+// what their owners publish); every wait therefore ends.  finish_kernel reads
+// what stream_kernel wrote after the kernel boundary.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -56,72 +68,74 @@
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kPerThread = 32;                 // logits per thread per row
-constexpr int kChunk = kThreads * kPerThread;  // 8192 logits per chunk
-constexpr int kMaxChunks = 64;                 // V <= 524288
+constexpr int kStreamWaves = 4;                // independent waves per stream workgroup
+constexpr int kStreamThreads = 64 * kStreamWaves;
+constexpr int kU = 4;                          // 16-byte loads per lane and row of an item
+constexpr int kRowBytes = kU * 64 * 16;        // bytes of one row in one item (4 KB)
+constexpr int kMaxChunks = 256;                // chunks per fp32 row (V <= 262144)
+constexpr int kMaxChunksBf16 = 128;            // chunks per bf16 row (V <= 262144)
 constexpr int kGroups = 8;                     // row groups = XCDs of an MI355X
-constexpr int kHalf = 32;                      // lanes per sub-chunk
-constexpr int kHalves = kThreads / kHalf;      // sub-chunks per load round
-constexpr int kMaxSub = 64;                    // sub-chunks per chunk (fp32 64, bf16 32)
-constexpr int kX1 = 4;                         // exchange-1 slots per chunk
-constexpr int kPart = 4 + 2 * kMaxSub;         // floats of partials per chunk
+constexpr int kX1 = 4;                         // exchange slots per (row, chunk)
+constexpr int kPart = 4;                       // floats of partials per (row, chunk)
 constexpr int kMaxGamma = 255;                 // rows per sequence <= 256
-constexpr int kFinishWaves = 16;
-constexpr int kDefaultSpin = 1 << 18;          // ~0.3 s of polling; normal waits are microseconds
+constexpr int kFinishWaves = 8;
+constexpr int kLayoutThreads = 1024;
+constexpr int kDefaultSpin = 64;               // polls (~1 us each) before a wave computes missing chunks itself
+constexpr int kMaxSpin = 1 << 20;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFltMin = 1.17549435e-38f;
 constexpr float kFltMax = 3.40282347e38f;
 constexpr uint32_t kTokMask = (1u << 23) - 1;
 constexpr uint32_t kAccBit = 1u << 23;
 constexpr uint32_t kStatusShift = 24;          // 0 ok, 1 invalid data, 2 wait expired
+constexpr int kRsrcWord3 = 0x00020000;         // raw (untyped) buffer, gfx9 family
+constexpr int kNT = 2;                         // buffer-load cache policy: nontemporal
 
-// partials of one (row, chunk), floats
-constexpr int kPDone = 0;                      // epoch that completed the item (bits)
-constexpr int kPW = 1;                         // sum of max(0, e_t - rho e_d)
-constexpr int kPB = 2;                         // sum of min(e_t, rho e_d)
-constexpr int kPWsub = 4;                      // [kMaxSub] residual sub-chunk sums
-constexpr int kPPsub = 4 + kMaxSub;            // [kMaxSub] sub-chunk sums of e_t
+// Partials of one (row, chunk), kPart floats: the epoch that completed the
+// item (bits), the sum of e_t - min(e_t, rho e_d), the sum of
+// min(e_t, rho e_d), unused.
 
 template <int DT> struct Fmt;
 template <> struct Fmt<SPECVERIFY_F32> {
   static constexpr int EPV = 4;   // logits per 16-byte vector
-  static constexpr int U = 8;     // vectors per thread per row
   static constexpr int ESIZE = 4;
+  static constexpr int L = kU * EPV;   // logits per lane and row of an item
+  static constexpr int CH = 64 * L;    // logits per chunk
 };
 template <> struct Fmt<SPECVERIFY_BF16> {
   static constexpr int EPV = 8;
-  static constexpr int U = 4;
   static constexpr int ESIZE = 2;
+  static constexpr int L = kU * EPV;
+  static constexpr int CH = 64 * L;
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 struct Params {
-  const void* target;
-  const void* draft;
-  int64_t tstride;
-  int64_t dstride;
+  const char* target;
+  const char* draft;
+  int64_t tstride_b;         // row strides in bytes
+  int64_t dstride_b;
   const int32_t* tokens;
   const float* uniforms;
   const float* temps;
   const int32_t* cu_draft;   // NULL: uniform gamma
+  const int4* rowinfo;       // ragged: per target row {sequence (<0: bad layout), draft row, has draft, T bits}
+  const uint32_t* layout;    // ragged: epoch * 2 + (layout invalid)
   int32_t gamma;
   int32_t B;
   int32_t R_d;
   int32_t R_t;
   int32_t V;
   int32_t C;                 // chunks per row
-  int32_t G;                 // stream workgroups per row group
+  int32_t Gw;                // stream waves per row group
   int32_t max_gamma;
   uint32_t epoch;
   int32_t spin_limit;
-  int32_t t_aligned;         // target rows start on 16-byte boundaries
-  int32_t d_aligned;
   uint64_t* xch1;            // [rows][C][kX1] tagged slots
+  uint64_t* dummy;           // [stream waves][8]: where a wave's step with nothing to publish writes
   float* part;               // [rows][C][kPart]
-  float* rowpart;            // [rows][2]: p(x), q(x)
   int32_t* acc_len;
   int32_t* out_tokens;
   float* p_draft;
@@ -132,29 +146,26 @@ struct Params {
 
 // ------------------------------------------------------------------ slots
 
+// One 64-bit store (single-copy atomic); the CU's L1 writes it through to
+// the XCD's L2, where the sc0 loads of the other waves of the row find it.
 __device__ __forceinline__ void slot_put(uint64_t* p, uint32_t tag, uint32_t v) {
-  __hip_atomic_store(p, ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  *p = ((uint64_t)tag << 32) | v;
 }
-// Poll one slot until it carries `tag`; false once `limit` polls have failed.
-__device__ __forceinline__ bool slot_get(uint64_t* p, uint32_t tag, int limit, uint32_t& v) {
-  for (int k = 0;; ++k) {
-    const uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)(w >> 32) == tag) {
-      v = (uint32_t)w;
-      return true;
-    }
-    if (k >= limit) return false;
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
+__device__ __forceinline__ uint32_t slot_tag(uint64_t w) { return (uint32_t)(w >> 32); }
+__device__ __forceinline__ float slot_f(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
 // ------------------------------------------------------------------ wave primitives (DPP)
-// Reductions leave the same value in every lane and use a fixed order, so
-// the two kernels, and every workgroup, reduce the same data to the same bits.
+// Reductions use a fixed order, so the two kernels, and every wave, reduce
+// the same data to the same bits.
 
-template <int CTRL, int ROW_MASK = 0xf>
+template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_rows(float v, float fill) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v), CTRL, ROW_MASK,
+                                                    0xf, false));
 }
 template <int CTRL>
 __device__ __forceinline__ int dppi(int v) {
@@ -163,24 +174,39 @@ __device__ __forceinline__ int dppi(int v) {
 __device__ __forceinline__ float lane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
-// Sums of the four 16-lane rows, left in every lane of each row.
-__device__ __forceinline__ float row_sum16(float v) {
+// Sum over the 64 lanes: a butterfly inside each 16-lane row, then
+// row_bcast:15 and row_bcast:31 fold the rows as (r3 + r2) + (r1 + r0).
+__device__ __forceinline__ float wave_sum(float v) {
   v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
   v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
   v += dpp<0x141>(v);   // row_half_mirror
   v += dpp<0x140>(v);   // row_mirror
-  return v;
+  v += dpp_rows<0x142, 0xa>(v, 0.0f);   // rows 1, 3 += last lane of rows 0, 2
+  v += dpp_rows<0x143, 0xc>(v, 0.0f);   // rows 2, 3 += lane 31
+  return lane_f(v, 63);
 }
-__device__ __forceinline__ float wave_sum(float v) {
-  v = row_sum16(v);
-  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+// Max over the 64 lanes on order-preserving integer keys of the floats
+// (integer max needs no NaN quieting, so each step is one DPP max); a
+// positive NaN would win, which only makes an invalid row invalid.
+__device__ __forceinline__ int f2key(float f) {
+  const int b = __float_as_int(f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
 }
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  v = fmaxf(v, dpp<0x140>(v));
-  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+__device__ __forceinline__ float key2f(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+template <int CTRL>
+__device__ __forceinline__ int dpp_all(int v) {    // every lane has a source lane
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, true);
+}
+__device__ __forceinline__ float wave_max(float f) {
+  int v = f2key(f);
+  v = max(v, dpp_all<0xB1>(v));
+  v = max(v, dpp_all<0x4E>(v));
+  v = max(v, dpp_all<0x141>(v));
+  v = max(v, dpp_all<0x140>(v));
+  // every lane holds its row's max: fold the four rows on the scalar unit
+  const int a = max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16));
+  const int b = max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48));
+  return key2f(max(a, b));
 }
 // Inclusive prefix sum over the 64 lanes, fixed association.
 __device__ __forceinline__ float wave_scan(float v, int lane) {
@@ -235,14 +261,6 @@ __device__ __forceinline__ void wave_argmax(float& v, int& k) {
   k = bk;
 }
 
-// Row normalisers of a softmax split into chunks: lane c (< C) holds chunk c's
-// (max m, sum s of 2^(l s_T - m s_T)); the merge is (max, sum 2^((m - M) s_T)).
-// Both kernels call this with the same lane layout.
-__device__ __forceinline__ void merge_chunks(float m, float sum, bool in, float sT, float& M, float& S) {
-  M = wave_max(in ? m : -__builtin_huge_valf());
-  S = wave_sum(in ? sum * __builtin_amdgcn_exp2f((m - M) * sT) : 0.0f);
-}
-
 // Exponent offset of a chunk: -m s, or 0 for a chunk of only -inf (so that
 // its exponentials are 2^-inf = 0 instead of NaN).
 __device__ __forceinline__ float chunk_offset(float m, float s) {
@@ -253,89 +271,123 @@ __device__ __forceinline__ float chunk_scale(float m, float M, float S, float s)
   return __builtin_amdgcn_exp2f((m - M) * s) / S;
 }
 // Weight of one logit pair in the residual, in the chunk's units; the stream
-// and finish kernels both use this (built without fp contraction) so the
-// finisher's re-scan sees the stream kernel's bits.
+// and finish kernels compute it with the same operations (built without fp
+// contraction), so the finisher's re-scan sees the stream kernel's bits.
 __device__ __forceinline__ float resid_w(float et, float ed, float rho) {
-  return fmaxf(et - rho * ed, 0.0f);
+  return et - fminf(et, rho * ed);
+}
+
+// ------------------------------------------------------------------ chunk slots of a row
+
+// The exchange slots of every chunk of row r, lane-major: lane l holds
+// chunks l, l + 64, ...  Lanes past the last chunk read the dummy slots.
+template <int NPER>
+struct RowSlots {
+  uint64_t w[NPER][kX1];
+};
+// Byte offsets of a lane's slots inside a row (loop invariant; lanes past
+// the last chunk re-read the last one, whose values they never use).
+template <int NPER>
+__device__ __forceinline__ void slot_offsets(int C, int lane, uint32_t (&off)[NPER]) {
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) off[j] = (uint32_t)min(lane + 64 * j, C - 1) * (kX1 * sizeof(uint64_t));
+}
+// The slots of row r, read with 64-bit buffer loads that miss the CU's L1
+// (sc0) and are served by the XCD's L2, through a buffer over the row's slots:
+// a uniform base and loop-invariant lane offsets, so no vector register is
+// written before the loads issue.  `real` false: a zero-sized buffer, the
+// loads read zeros (tag 0 is never an epoch) and touch no memory.
+constexpr int kSC0 = 16;   // sc1: the load misses L1 and reads L2
+template <int NPER>
+__device__ __forceinline__ void slots_issue(const Params& P, int r, bool real, const uint32_t (&off)[NPER],
+                                            RowSlots<NPER>& q) {
+  const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc((void*)(P.xch1 + (int64_t)(real ? r : 0) * P.C * kX1),
+                                                    (short)0, real ? P.C * kX1 * (int)sizeof(uint64_t) : 0,
+                                                    kRsrcWord3);
+#pragma unroll
+  for (int j = 0; j < NPER; ++j)
+#pragma unroll
+    for (int k = 0; k < kX1; ++k) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, off[j] + k * 8, 0, kSC0);
+      q.w[j][k] = (uint64_t)v[0] | ((uint64_t)v[1] << 32);
+    }
+}
+// Every chunk's first `n` slots carry `tag` (wave-uniform answer).
+template <int NPER>
+__device__ __forceinline__ bool slots_ready(const RowSlots<NPER>& q, int C, uint32_t tag, int n, int lane) {
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j)
+    if (lane + 64 * j < C) {
+#pragma unroll
+      for (int k = 0; k < kX1; ++k)
+        if (k < n) ok &= slot_tag(q.w[j][k]) == tag;
+    }
+  return __all(ok);
+}
+// Row normalisers of a softmax split into chunks from slots (m_c, s_c) at
+// slot index `at`: M = max m_c, S = sum s_c 2^((m_c - M) s).  Both kernels
+// call this with the same lane layout.
+template <int NPER>
+__device__ __forceinline__ void merge_row(const RowSlots<NPER>& q, int C, int at, float s, int lane, float& M,
+                                          float& S) {
+  float m = -__builtin_huge_valf();
+#pragma unroll
+  for (int j = 0; j < NPER; ++j)
+    if (lane + 64 * j < C) m = fmaxf(m, slot_f(q.w[j][at]));
+  M = wave_max(m);
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j)
+    if (lane + 64 * j < C) a += slot_f(q.w[j][at + 1]) * __builtin_amdgcn_exp2f((slot_f(q.w[j][at]) - M) * s);
+  S = wave_sum(a);
+}
+__device__ __forceinline__ bool norm_ok(float M, float S) {
+  return M > -__builtin_huge_valf() && S == S && S > 0.0f && S <= kFltMax;
 }
 
 // ------------------------------------------------------------------ loads
 
-// Issue this thread's loads of one chunk row: vector u holds tokens
-// e0 + u*256*EPV + tid*EPV .. +EPV-1.  Tokens >= V read as -inf; rows not on
-// 16-byte boundaries are read element by element.
-template <int DT>
-__device__ __forceinline__ void issue_chunk(const void* base, int64_t row, int64_t stride, int64_t e0,
-                                            int V, int tid, bool aligned, u32x4 (&raw)[Fmt<DT>::U]) {
+__device__ __forceinline__ Rsrc row_rsrc(const char* base, int64_t row, int64_t stride_b, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row * stride_b), (short)0, nbytes, kRsrcWord3);
+}
+
+// Loads of one row of chunk c: vector u of lane `lane` holds tokens
+// c*CH + u*64*EPV + lane*EPV .. +EPV-1.  VEC: 16-byte loads (rows and V*esize
+// on 16-byte boundaries); otherwise element loads.  Bytes past the buffer
+// read as 0 (the caller turns tokens >= V into -inf).
+template <int DT, bool VEC>
+__device__ __forceinline__ u32x4 load_vec(Rsrc rs, int c, int u, int lane) {
   using F = Fmt<DT>;
-  const char* rowp = (const char*)base + row * stride * F::ESIZE;
-  if (aligned && e0 + kChunk <= V) {
+  u32x4 w;
+  if (VEC) {
+    // the lane's offset is loop invariant; the chunk's goes into the scalar offset
+    w = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + u * 1024, c * kRowBytes, kNT);
+  } else {
+    const int t0 = c * F::CH + u * 64 * F::EPV + lane * F::EPV;
 #pragma unroll
-    for (int u = 0; u < F::U; ++u) {
-      const int64_t k = e0 + (int64_t)u * kThreads * F::EPV + (int64_t)tid * F::EPV;
-      raw[u] = __builtin_nontemporal_load((const u32x4*)(rowp + k * F::ESIZE));
-    }
-    return;
-  }
-#pragma unroll
-  for (int u = 0; u < F::U; ++u) {
-    const int64_t k = e0 + (int64_t)u * kThreads * F::EPV + (int64_t)tid * F::EPV;
-    if (aligned && k + F::EPV <= V) {
-      raw[u] = __builtin_nontemporal_load((const u32x4*)(rowp + k * F::ESIZE));
-    } else if (DT == SPECVERIFY_F32) {
-      const uint32_t* p = (const uint32_t*)rowp;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) raw[u][e] = (k + e < V) ? p[k + e] : 0xFF800000u;
-    } else {
-      const uint16_t* p = (const uint16_t*)rowp;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (k + 2 * e < V) ? p[k + 2 * e] : 0xFF80u;
-        const uint32_t hi = (k + 2 * e + 1 < V) ? p[k + 2 * e + 1] : 0xFF80u;
-        raw[u][e] = lo | (hi << 16);
+    for (int e = 0; e < 4; ++e) {
+      if (DT == SPECVERIFY_F32) {
+        w[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, (t0 + e) * 4, 0, kNT);
+      } else {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, (t0 + 2 * e) * 2, 0, kNT);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, (t0 + 2 * e + 1) * 2, 0, kNT);
+        w[e] = lo | (hi << 16);
       }
     }
   }
+  return w;
 }
-
-// EPV logits starting at token k (fewer near V: -inf), as fp32.
-template <int DT>
-__device__ __forceinline__ void load_group(const void* base, int64_t row, int64_t stride, int64_t k,
-                                           int V, bool aligned, float (&x)[Fmt<DT>::EPV]) {
-  using F = Fmt<DT>;
-  const char* rowp = (const char*)base + row * stride * F::ESIZE;
-  u32x4 raw;
-  if (aligned && k + F::EPV <= V) {
-    raw = *(const u32x4*)(rowp + k * F::ESIZE);
-  } else if (DT == SPECVERIFY_F32) {
-    const uint32_t* p = (const uint32_t*)rowp;
+template <int DT, bool VEC>
+__device__ __forceinline__ void issue_row(Rsrc rs, int c, int lane, u32x4 (&raw)[kU]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) raw[e] = (k + e < V) ? p[k + e] : 0xFF800000u;
-  } else {
-    const uint16_t* p = (const uint16_t*)rowp;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = (k + 2 * e < V) ? p[k + 2 * e] : 0xFF80u;
-      const uint32_t hi = (k + 2 * e + 1 < V) ? p[k + 2 * e + 1] : 0xFF80u;
-      raw[e] = lo | (hi << 16);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (DT == SPECVERIFY_F32) {
-      x[e] = __uint_as_float(raw[e]);
-    } else {
-      x[2 * e] = __uint_as_float(raw[e] << 16);
-      x[2 * e + 1] = __uint_as_float(raw[e] & 0xFFFF0000u);
-    }
-  }
+  for (int u = 0; u < kU; ++u) raw[u] = load_vec<DT, VEC>(rs, c, u, lane);
 }
 
 template <int DT>
-__device__ __forceinline__ void unpack(const u32x4 (&raw)[Fmt<DT>::U], float (&x)[kPerThread]) {
-  using F = Fmt<DT>;
+__device__ __forceinline__ void unpack(const u32x4 (&raw)[kU], float (&x)[Fmt<DT>::L]) {
 #pragma unroll
-  for (int u = 0; u < F::U; ++u) {
+  for (int u = 0; u < kU; ++u) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t w = raw[u][e];
@@ -348,357 +400,433 @@ __device__ __forceinline__ void unpack(const u32x4 (&raw)[Fmt<DT>::U], float (&x
     }
   }
 }
+// Tokens >= V of the last chunk become -inf.
+template <int DT>
+__device__ __forceinline__ void mask_tail(float (&x)[Fmt<DT>::L], int c, int V, int lane) {
+  using F = Fmt<DT>;
+  const int t0 = c * F::CH + lane * F::EPV;
+#pragma unroll
+  for (int u = 0; u < kU; ++u)
+#pragma unroll
+    for (int e = 0; e < F::EPV; ++e)
+      if (t0 + u * 64 * F::EPV + e >= V) x[u * F::EPV + e] = -__builtin_huge_valf();
+}
+// Token of element (u, e) of a lane.
+template <int DT>
+__device__ __forceinline__ int token_of(int c, int k, int lane) {
+  using F = Fmt<DT>;
+  const int u = k / F::EPV, e = k - u * F::EPV;
+  return c * F::CH + u * 64 * F::EPV + lane * F::EPV + e;
+}
+// Element e of vector u of a lane, as unpack and mask_tail leave it; `lim`
+// is V minus the token of element 0 of the vector (tokens >= V are -inf).
+template <int DT>
+__device__ __forceinline__ float elem(const u32x4& w, int e, int lim) {
+  float x;
+  if (DT == SPECVERIFY_F32) {
+    x = __uint_as_float(w[e]);
+  } else {
+    const uint32_t h = w[e >> 1];
+    x = __uint_as_float((e & 1) ? (h & 0xFFFF0000u) : (h << 16));
+  }
+  return e >= lim ? -__builtin_huge_valf() : x;
+}
 
 // ------------------------------------------------------------------ sequence layout
 
-struct Seq {
-  int b, gam, d0;
-  bool ok;
+// Read-only inputs that a wave reads at a uniform address go through the
+// constant address space, so they become scalar loads (counted apart from
+// the vector loads that the pipeline keeps in flight).
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
+struct RowMeta {
+  int b;      // sequence (< 0: the batch layout is invalid)
+  int rd;     // draft row
+  int pair;   // position has a draft
+  float T;
 };
-// The sequence owning target row r (binary search of cu_t[b] = cu_draft[b] + b).
-__device__ __forceinline__ Seq seq_of_row(const Params& P, int r) {
-  Seq q;
-  if (P.cu_draft == nullptr) {
-    q.b = r / (P.gamma + 1);
-    q.gam = P.gamma;
-    q.d0 = q.b * P.gamma;
+__device__ __forceinline__ RowMeta row_meta(const Params& P, int r) {
+  RowMeta m;
+  if (P.rowinfo == nullptr) {
+    const int g1 = P.gamma + 1;
+    m.b = r / g1;
+    const int i = r - m.b * g1;
+    m.pair = i < P.gamma;
+    m.rd = m.b * P.gamma + i;
+    m.T = ld_const(P.temps, m.b);
   } else {
-    int lo = 0, hi = P.B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (P.cu_draft[mid] + mid <= r) lo = mid;
-      else hi = mid - 1;
-    }
-    q.b = lo;
-    q.d0 = P.cu_draft[lo];
-    q.gam = P.cu_draft[lo + 1] - q.d0;
+    const int* info = (const int*)(P.rowinfo + r);
+    m.b = ld_const(info, 0);
+    m.rd = ld_const(info, 1);
+    m.pair = ld_const(info, 2);
+    m.T = __int_as_float(ld_const(info, 3));
   }
-  const int i = r - (q.d0 + q.b);
-  q.ok = q.gam >= 0 && q.gam <= P.max_gamma && q.d0 >= 0 && q.d0 + q.gam <= P.R_d && i >= 0 && i <= q.gam;
-  return q;
+  return m;
+}
+__device__ __forceinline__ bool t_sampled(float T) { return T >= kFltMin && T <= kFltMax; }
+
+// ================================================================== layout kernel (ragged batches)
+
+// One workgroup: checks that cu_draft is a layout (cu_draft[0] = 0,
+// cu_draft[B] = R_d, 0 <= gamma_b <= max_gamma) and writes every target row's
+// record; an invalid layout marks every row.
+__global__ __launch_bounds__(kLayoutThreads) void layout_kernel(Params P, int4* rowinfo, uint32_t* flag) {
+  const int tid = threadIdx.x;
+  int bad = 0;
+  for (int b = tid; b < P.B; b += blockDim.x) {
+    const int g = P.cu_draft[b + 1] - P.cu_draft[b];
+    bad |= g < 0 || g > P.max_gamma;
+  }
+  if (tid == 0) bad |= P.cu_draft[0] != 0 || P.cu_draft[P.B] != P.R_d;
+  bad = __syncthreads_or(bad);
+  if (bad) {
+    for (int r = tid; r < P.R_t; r += blockDim.x) rowinfo[r] = make_int4(-1, 0, 0, 0);
+  } else {
+    for (int b = tid; b < P.B; b += blockDim.x) {
+      const int d0 = P.cu_draft[b], g = P.cu_draft[b + 1] - d0;
+      const int Tb = __float_as_int(P.temps[b]);
+      for (int i = 0; i <= g; ++i) rowinfo[d0 + b + i] = make_int4(b, d0 + i, i < g ? 1 : 0, Tb);
+    }
+  }
+  if (tid == 0) *flag = P.epoch * 2u + (bad ? 1u : 0u);
 }
 
 // ================================================================== stream kernel
 
 struct Item {
-  int r, c;       // target row, chunk
-  int b, i, rd;   // sequence, position, draft row
-  bool ok, pair;
-  float T;
-  int xtok;
+  int r, c;   // target row (< 0: no item), chunk
+  int rd;     // draft row
+  int mode;   // 0 nothing to do, 1 sampled, 2 greedy
+  int pair;   // position has a draft
+  float s;    // log2(e) / T
 };
 
-__device__ __forceinline__ void item_place(const Params& P, int grp, int idx, Item& it) {
+__device__ __forceinline__ Item make_item(const Params& P, int grp, int idx, int n_items) {
+  Item it;
+  it.r = -1;
+  it.c = 0;
+  it.rd = 0;
+  it.mode = 0;
+  it.pair = 0;
+  it.s = 0.0f;
+  if (idx >= n_items) return it;
   const int rl = idx / P.C;
   it.c = idx - rl * P.C;
-  it.r = rl * kGroups + grp;
-}
-// Sequence of the item's row and its per-row scalars; the loads overlap the
-// work on the current item.
-__device__ __forceinline__ void item_lookup(const Params& P, Item& it) {
-  const Seq q = seq_of_row(P, it.r);
-  it.b = q.b;
-  it.i = it.r - (q.d0 + q.b);
-  it.rd = q.d0 + it.i;
-  it.ok = q.ok;
-  it.pair = q.ok && it.i < q.gam;
-  it.T = q.ok ? P.temps[q.b] : 0.0f;
-  it.xtok = it.pair ? P.tokens[it.rd] : 0;
-}
-
-struct StreamShared {
-  float red[2 * kWaves];
-  int redi[2 * kWaves];
-  uint32_t x1[kX1 * kMaxChunks];
-  float Mt, St, Md, Sd;
-};
-
-__device__ __forceinline__ void block_max2(float& a, float& b, StreamShared& sh) {
-  a = wave_max(a);
-  b = wave_max(b);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    sh.red[w] = a;
-    sh.red[kWaves + w] = b;
-  }
-  __syncthreads();
-  a = fmaxf(fmaxf(sh.red[0], sh.red[1]), fmaxf(sh.red[2], sh.red[3]));
-  b = fmaxf(fmaxf(sh.red[4], sh.red[5]), fmaxf(sh.red[6], sh.red[7]));
-  __syncthreads();
-}
-__device__ __forceinline__ void block_sum2(float& a, float& b, StreamShared& sh) {
-  a = wave_sum(a);
-  b = wave_sum(b);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    sh.red[w] = a;
-    sh.red[kWaves + w] = b;
-  }
-  __syncthreads();
-  a = (sh.red[0] + sh.red[1]) + (sh.red[2] + sh.red[3]);
-  b = (sh.red[4] + sh.red[5]) + (sh.red[6] + sh.red[7]);
-  __syncthreads();
-}
-__device__ __forceinline__ void block_argmax(float& v, int& k, StreamShared& sh) {
-  wave_argmax(v, k);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    sh.red[w] = v;
-    sh.redi[w] = k;
-  }
-  __syncthreads();
-  v = sh.red[0];
-  k = sh.redi[0];
-#pragma unroll
-  for (int j = 1; j < kWaves; ++j) argmax_merge(v, k, sh.red[j], sh.redi[j]);
-  __syncthreads();
+  it.r = grp + kGroups * rl;
+  const RowMeta m = row_meta(P, it.r);
+  if (m.b < 0) return it;   // invalid layout: nothing is read
+  it.rd = m.rd;
+  it.pair = m.pair;
+  if (t_sampled(m.T)) {
+    it.mode = 1;
+    it.s = kLog2e / m.T;
+  } else if (m.T == 0.0f) {
+    it.mode = 2;
+  }   // any other temperature is invalid data: nothing is read
+  return it;
 }
 
-// Sums over each 32-lane half of the wave; lane 0 of the wave writes the two
-// halves of the u-th load round to dst[u * kHalves + 2 * wave + {0, 1}].
-__device__ __forceinline__ void store_halves(float v, float* dst, int u) {
-  const float r = row_sum16(v);
-  const float h0 = lane_f(r, 0) + lane_f(r, 16);
-  const float h1 = lane_f(r, 32) + lane_f(r, 48);
-  if ((threadIdx.x & 63) == 0) {
-    const int w = threadIdx.x >> 6;
-    dst[u * kHalves + 2 * w] = h0;
-    dst[u * kHalves + 2 * w + 1] = h1;
-  }
+// The item's loads: always the same 2 kU (VEC) instructions; absent rows
+// read through zero-sized buffers.
+template <int DT, bool VEC>
+__device__ __forceinline__ void issue_item(const Params& P, const Item& it, int lane, u32x4 (&R)[2][kU]) {
+  const int nb = P.V * Fmt<DT>::ESIZE;
+  const bool live = it.r >= 0 && it.mode != 0;
+  const Rsrc rt = row_rsrc(P.target, live ? it.r : 0, P.tstride_b, live ? nb : 0);
+  const Rsrc rd = row_rsrc(P.draft, (live && it.pair) ? it.rd : 0, P.dstride_b, (live && it.pair) ? nb : 0);
+  issue_row<DT, VEC>(rt, it.c, lane, R[0]);
+  issue_row<DT, VEC>(rd, it.c, lane, R[1]);
 }
 
-// Per-thread argmax of a chunk in token order (first maximum wins) plus a
-// flag for NaN / +inf.
+// Phase 1 of a sampled row: chunk max, exponentials in place, chunk sum.
 template <int DT>
-__device__ __forceinline__ void thread_argmax(const float (&x)[kPerThread], int64_t e0, int tid,
-                                              float& bv, int& bk, int& bad) {
-  using F = Fmt<DT>;
-  bv = -__builtin_huge_valf();
-  int slot = -1;
+__device__ __forceinline__ void p1_row(float (&x)[Fmt<DT>::L], float s, float& m, float& sum) {
+  float mm = -__builtin_huge_valf();
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const float v = x[k];
-    bad |= (v != v) | (v == __builtin_huge_valf());
-    if (v > bv) {
-      bv = v;
-      slot = k;
+  for (int k = 0; k < Fmt<DT>::L; ++k) mm = fmaxf(mm, x[k]);
+  m = wave_max(mm);
+  const float c = chunk_offset(m, s);
+  float a = 0.0f;
+#pragma unroll
+  for (int k = 0; k < Fmt<DT>::L; ++k) {
+    x[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k], s, c));
+    a += x[k];
+  }
+  sum = wave_sum(a);
+}
+
+// The statistics p1_row computes for chunk c of a row, read again from
+// memory one vector at a time (few registers; a rare path): the same
+// operations on the same values in the same order, hence the same bits.
+template <int DT, bool VEC>
+__device__ __forceinline__ void stats_mem(Rsrc rs, int c, int V, int lane, float s, float& m, float& sum) {
+  using F = Fmt<DT>;
+  const int lim0 = V - (c * F::CH + lane * F::EPV);
+  float mm = -__builtin_huge_valf();
+#pragma unroll 1
+  for (int u = 0; u < kU; ++u) {
+    const u32x4 w = load_vec<DT, VEC>(rs, c, u, lane);
+    const int lim = lim0 - u * 64 * F::EPV;
+#pragma unroll
+    for (int e = 0; e < F::EPV; ++e) mm = fmaxf(mm, elem<DT>(w, e, lim));
+  }
+  m = wave_max(mm);
+  const float off = chunk_offset(m, s);
+  float a = 0.0f;
+#pragma unroll 1
+  for (int u = 0; u < kU; ++u) {
+    const u32x4 w = load_vec<DT, VEC>(rs, c, u, lane);
+    const int lim = lim0 - u * 64 * F::EPV;
+#pragma unroll
+    for (int e = 0; e < F::EPV; ++e) a += __builtin_amdgcn_exp2f(__builtin_fmaf(elem<DT>(w, e, lim), s, off));
+  }
+  sum = wave_sum(a);
+}
+
+// Chunk argmax of a greedy row (first maximum in token order) and a flag for
+// NaN / +inf.
+template <int DT>
+__device__ __forceinline__ void greedy_row(const float (&x)[Fmt<DT>::L], int c, int lane, float& v, int& k,
+                                           int& bad) {
+  float bv = -__builtin_huge_valf();
+  int slot = -1, b = 0;
+#pragma unroll
+  for (int j = 0; j < Fmt<DT>::L; ++j) {
+    const float y = x[j];
+    b |= (y != y) | (y == __builtin_huge_valf());
+    if (y > bv) {
+      bv = y;
+      slot = j;
     }
   }
-  const int u = slot / F::EPV, e = slot - u * F::EPV;
-  bk = slot < 0 ? 0x7FFFFFFF : (int)(e0 + u * (kThreads * F::EPV) + tid * F::EPV + e);
+  int bk = slot < 0 ? 0x7FFFFFFF : token_of<DT>(c, slot, lane);
+  wave_argmax(bv, bk);
+  v = bv;
+  k = bk;
+  bad = __any(b);
 }
 
-// Greedy rows (T = 0, or an invalid temperature that only needs reporting):
-// chunk argmax of target and draft into the exchange-1 slots.
+// Phase 1 of an item; publishes the chunk statistics.  `mt`, `md` keep the
+// chunk maxima for phase 2.
+// Both rows are unpacked whatever the item is, so that on every path the
+// compiler sees the item's loads consumed here and never waits for them
+// later (rows that were not read hold zeros).  Likewise every path ends in
+// the same one store (items with nothing to publish write the dummy slots),
+// so the count of memory operations in flight is the same on all paths.
 template <int DT>
-__device__ __forceinline__ void stream_greedy(const Params& P, const Item& it, const float (&xt)[kPerThread],
-                                              const float (&xd)[kPerThread], StreamShared& sh) {
-  const int tid = threadIdx.x;
-  const int64_t e0 = (int64_t)it.c * kChunk;
-  float vt, vd = -__builtin_huge_valf();
-  int kt, kd = 0x7FFFFFFF, badt = 0, badd = 0;
-  thread_argmax<DT>(xt, e0, tid, vt, kt, badt);
-  if (it.pair) thread_argmax<DT>(xd, e0, tid, vd, kd, badd);
-  badt = __syncthreads_or(badt);
-  badd = __syncthreads_or(badd);
-  block_argmax(vt, kt, sh);
-  if (it.pair) block_argmax(vd, kd, sh);
-  if (tid < kX1) {
-    const uint32_t v = tid == 0 ? __float_as_uint(vt) : tid == 1 ? (badt ? 0xFFFFFFFFu : (uint32_t)kt)
-                     : tid == 2 ? __float_as_uint(vd) : (badd ? 0xFFFFFFFFu : (uint32_t)kd);
-    slot_put(P.xch1 + ((int64_t)it.r * P.C + it.c) * kX1 + tid, P.epoch, v);
+__device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lane, uint64_t* wdummy,
+                                        const u32x4 (&R)[2][kU], float (&E)[2][Fmt<DT>::L], float& mt,
+                                        float& md) {
+  unpack<DT>(R[0], E[0]);
+  unpack<DT>(R[1], E[1]);
+  uint32_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
+  uint64_t* dst = wdummy;
+  if (it.mode != 0) {
+    dst = P.xch1 + ((int64_t)it.r * P.C + it.c) * kX1;
+    if ((it.c + 1) * Fmt<DT>::CH > P.V) {
+      mask_tail<DT>(E[0], it.c, P.V, lane);
+      mask_tail<DT>(E[1], it.c, P.V, lane);
+    }
+    if (it.mode == 1) {
+      float st, sd = 0.0f;
+      md = -__builtin_huge_valf();
+      p1_row<DT>(E[0], it.s, mt, st);
+      if (it.pair) p1_row<DT>(E[1], it.s, md, sd);
+      v0 = __float_as_uint(mt);
+      v1 = __float_as_uint(st);
+      v2 = __float_as_uint(md);
+      v3 = __float_as_uint(sd);
+    } else {
+      float vt, vd = -__builtin_huge_valf();
+      int kt, kd = 0x7FFFFFFF, bt, bd = 0;
+      greedy_row<DT>(E[0], it.c, lane, vt, kt, bt);
+      if (it.pair) greedy_row<DT>(E[1], it.c, lane, vd, kd, bd);
+      v0 = __float_as_uint(vt);
+      v1 = bt ? 0xFFFFFFFFu : (uint32_t)kt;
+      v2 = __float_as_uint(vd);
+      v3 = bd ? 0xFFFFFFFFu : (uint32_t)kd;
+    }
+  }
+  if (lane < kX1) {
+    const uint32_t v = lane == 0 ? v0 : lane == 1 ? v1 : lane == 2 ? v2 : v3;
+    slot_put(dst + lane, P.epoch, v);
   }
 }
 
-// Sampled rows (T > 0): phases 1 and 2 of one chunk.
-template <int DT>
-__device__ __forceinline__ void stream_sampled(const Params& P, const Item& it, float (&xt)[kPerThread],
-                                               float (&xd)[kPerThread], StreamShared& sh) {
-  using F = Fmt<DT>;
-  constexpr int EPV = F::EPV;
-  constexpr int U = F::U;
-  const int tid = threadIdx.x, lane = tid & 63, C = P.C;
+// A wave that has polled long enough for the slots of its row computes the
+// missing chunks' statistics itself (their owners may not even be running:
+// nothing guarantees that every workgroup of the grid is resident at once)
+// and publishes them; the owners later write the same bits.  The caller
+// polls again afterwards.
+template <int DT, bool VEC, int NPER>
+__device__ __forceinline__ void help_row(const Params& P, const Item& it, int lane, const RowSlots<NPER>& q) {
   const uint32_t tag = P.epoch;
-  const bool pair = it.pair;
-  uint64_t* x1row = P.xch1 + (int64_t)it.r * C * kX1;
-  float* part = P.part + ((int64_t)it.r * C + it.c) * kPart;
-  const float s = kLog2e / it.T;
-  const float ninf = -__builtin_huge_valf();
-
-  // ---- phase 1: chunk max, exponentials kept in registers, sums
-  float mt = ninf, md = ninf;
+  uint64_t miss[NPER];   // the slots are not needed past these masks
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) mt = fmaxf(mt, xt[k]);
-  if (pair) {
+  for (int j = 0; j < NPER; ++j) {
+    bool m = false;
+    if (lane + 64 * j < P.C) {
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) md = fmaxf(md, xd[k]);
-  }
-  block_max2(mt, md, sh);
-  const float ct = chunk_offset(mt, s);
-  const float cd = chunk_offset(md, s);
-  float gt[U];
-  float st = 0.0f, sd = 0.0f;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    float a = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      const int k = u * EPV + e;
-      xt[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(xt[k], s, ct));
-      a += xt[k];
+      for (int k = 0; k < kX1; ++k) m |= slot_tag(q.w[j][k]) != tag;
     }
-    gt[u] = a;
-    st += a;
+    miss[j] = __ballot(m);
   }
-  if (pair) {
+  const int nb = P.V * Fmt<DT>::ESIZE;
+  const Rsrc rt = row_rsrc(P.target, it.r, P.tstride_b, nb);
+  const Rsrc rd = row_rsrc(P.draft, it.rd, P.dstride_b, nb);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float a = 0.0f;
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const int k = u * EPV + e;
-        xd[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(xd[k], s, cd));
-        a += xd[k];
+  for (int j = 0; j < NPER; ++j) {
+    uint64_t mask = miss[j];
+    while (mask) {
+      const int c = __builtin_ctzll(mask) + 64 * j;
+      mask &= mask - 1;
+      float mt, st, md, sd;
+      stats_mem<DT, VEC>(rt, c, P.V, lane, it.s, mt, st);
+      stats_mem<DT, VEC>(rd, c, P.V, lane, it.s, md, sd);
+      if (lane < kX1) {
+        const uint32_t x = __float_as_uint(lane == 0 ? mt : lane == 1 ? st : lane == 2 ? md : sd);
+        slot_put(P.xch1 + ((int64_t)it.r * P.C + c) * kX1 + lane, tag, x);
       }
-      sd += a;
     }
-  }
-  block_sum2(st, sd, sh);
-  if (tid < kX1) {
-    const float v = tid == 0 ? mt : tid == 1 ? st : tid == 2 ? md : sd;
-    slot_put(x1row + (int64_t)it.c * kX1 + tid, tag, __float_as_uint(v));
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) store_halves(gt[u], part + kPPsub, u);
-  if (!pair) {
-    if (tid == 0) part[kPDone] = __uint_as_float(tag);
-    return;
-  }
-
-  // ---- exchange 1: the row's normalisers (M, S) of target and draft
-  int ok = 1;
-  if (tid < kX1 * C) {
-    uint32_t v = 0;
-    ok = slot_get(x1row + tid, tag, P.spin_limit, v);
-    sh.x1[tid] = v;
-  }
-  if (!__syncthreads_and(ok)) return;   // the finisher sees no completion mark and reports
-  if (tid < 64) {
-    const bool in = lane < C;
-    float Mt, St, Md, Sd;
-    merge_chunks(__uint_as_float(sh.x1[lane * kX1 + 0]), __uint_as_float(sh.x1[lane * kX1 + 1]), in, s, Mt, St);
-    merge_chunks(__uint_as_float(sh.x1[lane * kX1 + 2]), __uint_as_float(sh.x1[lane * kX1 + 3]), in, s, Md, Sd);
-    if (lane == 0) {
-      sh.Mt = Mt;
-      sh.St = St;
-      sh.Md = Md;
-      sh.Sd = Sd;
-    }
-  }
-  __syncthreads();
-  const float Mt = sh.Mt, St = sh.St, Md = sh.Md, Sd = sh.Sd;
-  const bool norm_ok = Mt > ninf && St == St && St > 0.0f && Md > ninf && Sd == Sd && Sd > 0.0f;
-  if (!norm_ok) {   // invalid data: the finisher reports it from the slots
-    if (tid == 0) part[kPDone] = __uint_as_float(tag);
-    return;
-  }
-  const float at = chunk_scale(mt, Mt, St, s);   // p_k = at e_t
-  const float ad = chunk_scale(md, Md, Sd, s);   // q_k = ad e_d
-  const float rho = ad / at;                     // q_k = at rho e_d
-
-  // ---- phase 2: sums of min(e_t, rho e_d) and max(0, e_t - rho e_d)
-  float wsub[U];
-  float bsum = 0.0f, wsum = 0.0f;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    float ws = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      const int k = u * EPV + e;
-      bsum += fminf(xt[k], rho * xd[k]);
-      ws += resid_w(xt[k], xd[k], rho);
-    }
-    wsub[u] = ws;
-    wsum += ws;
-  }
-  block_sum2(wsum, bsum, sh);
-#pragma unroll
-  for (int u = 0; u < U; ++u) store_halves(wsub[u], part + kPWsub, u);
-  // the chunk holding the drafted token: p(x) and q(x)
-  const int x = it.xtok;
-  if (x >= it.c * kChunk && x < (it.c + 1) * kChunk && x < P.V) {
-    const int loc = x - it.c * kChunk;
-    const int u = loc / (kThreads * EPV);
-    const int rem = loc - u * kThreads * EPV;
-    if (tid == rem / EPV) {
-      const int e = rem - (rem / EPV) * EPV;
-      float et = 0.0f, ed = 0.0f;
-#pragma unroll
-      for (int k = 0; k < kPerThread; ++k)
-        if (k == u * EPV + e) {
-          et = xt[k];
-          ed = xd[k];
-        }
-      P.rowpart[(int64_t)it.r * 2 + 0] = et * at;
-      P.rowpart[(int64_t)it.r * 2 + 1] = ed * ad;
-    }
-  }
-  if (tid == 0) {
-    part[kPW] = wsum;
-    part[kPB] = bsum;
-    part[kPDone] = __uint_as_float(tag);
   }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void stream_kernel(Params P) {
-  using F = Fmt<DT>;
-  __shared__ StreamShared sh;
-  const int tid = threadIdx.x;
-  const int grp = (int)(blockIdx.x % kGroups);
-  if (grp >= P.R_t) return;
-  const int n_items = ((P.R_t - grp + kGroups - 1) / kGroups) * P.C;
-  int idx = (int)(blockIdx.x / kGroups);
-  if (idx >= n_items) return;
-
-  Item it;
-  u32x4 rt[F::U], rdr[F::U];
-  item_place(P, grp, idx, it);
-  issue_chunk<DT>(P.target, it.r, P.tstride, (int64_t)it.c * kChunk, P.V, tid, P.t_aligned, rt);
-  item_lookup(P, it);
-  if (it.pair)
-    issue_chunk<DT>(P.draft, it.rd, P.dstride, (int64_t)it.c * kChunk, P.V, tid, P.d_aligned, rdr);
-  while (true) {
-    float xt[kPerThread], xd[kPerThread];
-    unpack<DT>(rt, xt);
-    if (it.pair) unpack<DT>(rdr, xd);
-    // prefetch the next item while this one is processed
-    const int nidx = idx + P.G;
-    const bool more = nidx < n_items;
-    Item nx = it;
-    if (more) {
-      item_place(P, grp, nidx, nx);
-      issue_chunk<DT>(P.target, nx.r, P.tstride, (int64_t)nx.c * kChunk, P.V, tid, P.t_aligned, rt);
-      item_lookup(P, nx);
-      if (nx.pair) issue_chunk<DT>(P.draft, nx.rd, P.dstride, (int64_t)nx.c * kChunk, P.V, tid, P.d_aligned, rdr);
+// Phase 2 of a sampled item with a draft, once its row's slots are in `q`
+// (`ready`: they all carry this run's tag).  Leaves the partials in `o` and
+// their address in `dst`; the caller stores them.
+template <int DT, bool VEC, int NPER>
+__device__ __forceinline__ void p2_item(const Params& P, const Item& it, int lane, const uint32_t (&soff)[NPER],
+                                        RowSlots<NPER>& q, bool ready,
+                                        const float (&E)[2][Fmt<DT>::L], float mt, float md, float4& o,
+                                        float*& dst) {
+  const uint32_t tag = P.epoch;
+  if (!ready) {
+    for (int k = 0;; ++k) {
+      // the help makes the next poll succeed; the bound only guards that
+      if (k > 2 * P.spin_limit + 16) return;   // no completion mark: the finisher reports it
+      if (k == P.spin_limit) {
+        help_row<DT, VEC, NPER>(P, it, lane, q);
+        __builtin_amdgcn_s_waitcnt(0);   // its stores are in L2 before the poll below
+      } else {
+        __builtin_amdgcn_s_sleep(2);
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the loads below are read again on every turn
+      slots_issue(P, it.r, true, soff, q);
+      if (slots_ready(q, P.C, tag, kX1, lane)) break;
     }
-    if (it.ok) {
-      __syncthreads();   // shared state of the previous item is no longer read
-      const bool sampled = it.T >= kFltMin && it.T <= kFltMax;
-      if (sampled) stream_sampled<DT>(P, it, xt, xd, sh);
-      else stream_greedy<DT>(P, it, xt, xd, sh);
-    }
-    if (!more) break;
-    idx = nidx;
-    it = nx;
   }
+  float Mt, St, Md, Sd;
+  merge_row(q, P.C, 0, it.s, lane, Mt, St);
+  merge_row(q, P.C, 2, it.s, lane, Md, Sd);
+  // invalid data gives NaN or inf here; the finisher checks the normalisers
+  const float at = chunk_scale(mt, Mt, St, it.s);   // p_k = at e_t
+  const float ad = chunk_scale(md, Md, Sd, it.s);   // q_k = ad e_d
+  const float rho = ad / at;                        // q_k = at rho e_d
+  float w = 0.0f, b = 0.0f;
+#pragma unroll
+  for (int k = 0; k < Fmt<DT>::L; ++k) {
+    const float mn = fminf(E[0][k], rho * E[1][k]);
+    b += mn;
+    w += E[0][k] - mn;
+  }
+  o.x = __uint_as_float(tag);
+  o.y = wave_sum(w);
+  o.z = wave_sum(b);
+  dst = P.part + ((int64_t)it.r * P.C + it.c) * kPart;
+}
+
+// One pipeline step, with the slots of `cur`'s row already in flight in q:
+//   phase 1 of n1 (its loads were issued two steps ago; exponentials into
+//   Efree), phase 2 of cur (exponentials in Ecur), then the poll of n1's
+//   row, then the loads of n3 into n1's buffer, now free.
+// The poll goes out before the loads: vector memory operations complete in
+// order, so waiting for the poll in the next step never waits for them.
+// Every path through a step issues the same memory operations (items that
+// do not exist read zero-sized buffers and write the dummy slots), so the
+// compiler's count of operations in flight is exact at every wait.
+// With more than 128 chunks per row the slots of a row take too many
+// registers to keep across phase 1: the poll is issued after it instead.
+template <int NPER>
+struct Poll {
+  static constexpr bool kLate = NPER > 2;
+};
+template <int DT, bool VEC, int NPER>
+__device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy, const uint32_t (&soff)[NPER],
+                                     RowSlots<NPER>& q,
+                                     const Item& cur, const float (&Ecur)[2][Fmt<DT>::L], float cmt, float cmd,
+                                     const Item& n1, u32x4 (&R1)[2][kU], float (&Efree)[2][Fmt<DT>::L], float& nmt,
+                                     float& nmd, const Item& n3) {
+  p1_item<DT>(P, n1, lane, wdummy, R1, Efree, nmt, nmd);
+  if (Poll<NPER>::kLate) slots_issue(P, cur.r, cur.mode == 1 && cur.pair, soff, q);
+  const bool ready = slots_ready(q, P.C, P.epoch, kX1, lane);   // consumes the poll on every path
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float* dst = (float*)(wdummy + kX1);
+  if (cur.mode == 1 && cur.pair) p2_item<DT, VEC, NPER>(P, cur, lane, soff, q, ready, Ecur, cmt, cmd, o, dst);
+  if (lane == 0) *(float4*)dst = o;
+  __builtin_amdgcn_sched_barrier(0);
+  if (!Poll<NPER>::kLate) slots_issue(P, n1.r, n1.mode == 1 && n1.pair, soff, q);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_item<DT, VEC>(P, n3, lane, R1);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int DT, bool VEC, int NPER>
+__global__ __launch_bounds__(kStreamThreads, 2) void stream_kernel(Params P) {
+  using F = Fmt<DT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = (int)(blockIdx.x % kGroups);
+  const int j = (int)(blockIdx.x / kGroups) * kStreamWaves + wave;
+  const int n_items = ((P.R_t - grp + kGroups - 1) / kGroups) * P.C;
+  if (j >= n_items) return;
+  const int G = P.Gw;
+  uint32_t soff[NPER];
+  slot_offsets(P.C, lane, soff);
+  // the wave's own dummy slots: waves never contend for a dummy cache line
+  uint64_t* wdummy = P.dummy + ((int64_t)blockIdx.x * kStreamWaves + wave) * 8;
+
+  u32x4 RA[2][kU], RB[2][kU];
+  float EA[2][F::L], EB[2][F::L];
+  float amt = 0.0f, amd = 0.0f, bmt = 0.0f, bmd = 0.0f;
+  RowSlots<NPER> q;
+  // prologue: items 0 and 1 in flight, phase 1 of item 0, its poll, item 2 in flight
+  Item ia = make_item(P, grp, j, n_items);
+  Item ib = make_item(P, grp, j + G, n_items);
+  issue_item<DT, VEC>(P, ia, lane, RA);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_item<DT, VEC>(P, ib, lane, RB);
+  __builtin_amdgcn_sched_barrier(0);
+  p1_item<DT>(P, ia, lane, wdummy, RA, EA, amt, amd);
+  __builtin_amdgcn_sched_barrier(0);
+  if (!Poll<NPER>::kLate) slots_issue(P, ia.r, ia.mode == 1 && ia.pair, soff, q);
+  __builtin_amdgcn_sched_barrier(0);
+  Item ic = make_item(P, grp, j + 2 * G, n_items);
+  issue_item<DT, VEC>(P, ic, lane, RA);
+  __builtin_amdgcn_sched_barrier(0);
+  // Two steps per turn, one exit at the top: when the first step's item is
+  // the wave's last, the second step runs on nothing (no waits, dummy writes).
+  for (int idx = j; idx < n_items; idx += 2 * G) {
+    // cur = ia (EA), n1 = ib (RB), n2 = ic (RA, in flight)
+    const Item id = make_item(P, grp, idx + 3 * G, n_items);
+    step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ia, EA, amt, amd, ib, RB, EB, bmt, bmd, id);
+    // cur = ib (EB), n1 = ic (RA), n2 = id (RB, in flight)
+    const Item ie = make_item(P, grp, idx + 4 * G, n_items);
+    step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ib, EB, bmt, bmd, ic, RA, EA, amt, amd, ie);
+    ia = ic;
+    ib = id;
+    ic = ie;
+  }
+  // loads of items past the end read zero-sized buffers; let them land
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // ================================================================== finish kernel
 
 struct FinishShared {
   uint32_t res[kMaxGamma + 1];   // row results of the sequence
-  int bad_layout;
 };
 
 __device__ __forceinline__ uint32_t row_payload(int status, bool acc, int tok) {
@@ -706,141 +834,188 @@ __device__ __forceinline__ uint32_t row_payload(int status, bool acc, int tok) {
          (status == 0 ? ((uint32_t)tok & kTokMask) : 0u);
 }
 
-// Owner selection over n <= 64 non-negative totals, one per lane: the first j
-// with tot_j > 0 and base + incl_j > thr, else the last j with tot_j > 0
-// (rounding guard).  Returns j (-1 if all are 0) and the CDF value before j.
-__device__ __forceinline__ int owner_select(float tot, int n, float base, float thr, int lane,
-                                            float& before) {
-  const float t = lane < n ? tot : 0.0f;
-  const float G = base + wave_scan(t, lane);
-  const uint64_t hit = __ballot(lane < n && t > 0.0f && G > thr);
-  const uint64_t pos = __ballot(lane < n && t > 0.0f);
-  int j;
-  if (hit) j = __builtin_ctzll(hit);
-  else if (pos) j = 63 - __builtin_clzll(pos);
-  else j = -1;
-  const float prev = lane_f(G, j > 0 ? j - 1 : 0);
-  before = j > 0 ? prev : base;
-  return j;
+template <int NPER>
+__device__ __forceinline__ float pick(const float (&a)[NPER], int j) {
+  float v = a[0];
+#pragma unroll
+  for (int i = 1; i < NPER; ++i)
+    if (i == j) v = a[i];
+  return v;
+}
+
+// One logit of a row as fp32 (token t < V).
+template <int DT>
+__device__ __forceinline__ float load_logit(const char* base, int64_t row, int64_t stride_b, int t) {
+  const char* p = base + row * stride_b;
+  if (DT == SPECVERIFY_F32) return ((const float*)p)[t];
+  return __uint_as_float((uint32_t)((const uint16_t*)p)[t] << 16);
 }
 
 // One row of a sampled sequence, on one wave.  Returns the row result.
-template <int DT>
-__device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int rd, bool pair, float T,
-                                                   float ui, float ug, int lane) {
+template <int DT, bool VEC, int NPER>
+__device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int rd, bool pair, float T, float ui,
+                                                   float ug, int lane) {
   using F = Fmt<DT>;
-  constexpr int EPV = F::EPV;
   const int C = P.C;
   const uint32_t tag = P.epoch;
   const float s = kLog2e / T;
   const float ninf = -__builtin_huge_valf();
-  const bool in = lane < C;
-  const int NSUB = kHalves * F::U;
-  // chunk statistics and partials
-  float m1 = ninf, s1 = 0.0f, m2 = ninf, s2 = 0.0f, W = 0.0f, Bs = 0.0f;
-  int ok = 1;
-  if (in) {
-    const uint64_t* x1 = P.xch1 + ((int64_t)r * C + lane) * kX1;
-    const uint64_t a = __hip_atomic_load(x1 + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t bb = __hip_atomic_load(x1 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t c = __hip_atomic_load(x1 + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t d = __hip_atomic_load(x1 + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ok = ((uint32_t)(a >> 32) == tag) & ((uint32_t)(bb >> 32) == tag) & ((uint32_t)(c >> 32) == tag) &
-         ((uint32_t)(d >> 32) == tag);
-    m1 = __uint_as_float((uint32_t)a);
-    s1 = __uint_as_float((uint32_t)bb);
-    m2 = __uint_as_float((uint32_t)c);
-    s2 = __uint_as_float((uint32_t)d);
-    const float* pt = P.part + ((int64_t)r * C + lane) * kPart;
-    ok &= __float_as_uint(pt[kPDone]) == tag;
-    W = pt[kPW];
-    Bs = pt[kPB];
+  const int x = pair ? ld_const(P.tokens, rd) : 0;
+  const bool x_ok = x >= 0 && x < P.V;
+  RowSlots<NPER> q;
+  uint32_t soff[NPER];
+  slot_offsets(C, lane, soff);
+  slots_issue(P, r, true, soff, q);
+  float W[NPER], Bp[NPER];
+  int done = 1;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    W[j] = 0.0f;
+    Bp[j] = 0.0f;
+    const int c = lane + 64 * j;
+    if (pair && c < C) {
+      const float4 pt = *(const float4*)(P.part + ((int64_t)r * C + c) * kPart);
+      done &= __float_as_uint(pt.x) == tag;
+      W[j] = pt.y;
+      Bp[j] = pt.z;
+    }
   }
-  if (!__all(ok)) return row_payload(2, false, 0);
+  float lx = 0.0f, dx = 0.0f;
+  if (pair && x_ok) {
+    lx = load_logit<DT>(P.target, r, P.tstride_b, x);
+    dx = load_logit<DT>(P.draft, rd, P.dstride_b, x);
+  }
+  if (!slots_ready(q, C, tag, pair ? 4 : 2, lane) || !__all(done)) return row_payload(2, false, 0);
   float Mt, St, Md = ninf, Sd = 0.0f;
-  merge_chunks(m1, s1, in, s, Mt, St);
-  if (pair) merge_chunks(m2, s2, in, s, Md, Sd);
-  const bool norm_ok = Mt > ninf && St == St && St > 0.0f &&
-                       (!pair || (Md > ninf && Sd == Sd && Sd > 0.0f));
-  const int x = pair ? P.tokens[rd] : 0;
-  if (!norm_ok || (pair && (x < 0 || x >= P.V))) return row_payload(1, false, 0);
-  // chunk scales, residual mass and beta
-  const float at = in ? chunk_scale(m1, Mt, St, s) : 0.0f;
-  const float ad = (in && pair) ? chunk_scale(m2, Md, Sd, s) : 0.0f;
-  const float rho = (in && pair) ? ad / at : 0.0f;
+  merge_row(q, C, 0, s, lane, Mt, St);
+  if (pair) merge_row(q, C, 2, s, lane, Md, Sd);
+  if (!norm_ok(Mt, St) || (pair && (!norm_ok(Md, Sd) || !x_ok))) return row_payload(1, false, 0);
+  // per-chunk scales, residual mass, beta, and the masses the final sample reads
+  float at[NPER], tot[NPER], mt[NPER], md[NPER], rho[NPER];
+  float zl = 0.0f, bl = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const bool in = lane + 64 * j < C;
+    mt[j] = in ? slot_f(q.w[j][0]) : ninf;
+    md[j] = (in && pair) ? slot_f(q.w[j][2]) : ninf;
+    at[j] = in ? chunk_scale(mt[j], Mt, St, s) : 0.0f;
+    const float ad = (in && pair) ? chunk_scale(md[j], Md, Sd, s) : 0.0f;
+    rho[j] = (in && pair) ? ad / at[j] : 0.0f;
+    zl += in ? at[j] * W[j] : 0.0f;
+    bl += in ? at[j] * Bp[j] : 0.0f;
+  }
   float Z = 0.0f, beta = 0.0f;
   if (pair) {
-    Z = wave_sum(in ? at * W : 0.0f);
-    beta = wave_sum(in ? at * Bs : 0.0f);
+    Z = wave_sum(zl);
+    beta = wave_sum(bl);
   }
   const bool resid = pair && Z > 0.0f;
-  const float tot = in ? (resid ? at * W : at * s1) : 0.0f;
-  const float mass = resid ? Z : wave_sum(tot);
+  float ml = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const bool in = lane + 64 * j < C;
+    tot[j] = !in ? 0.0f : resid ? at[j] * W[j] : at[j] * slot_f(q.w[j][1]);
+    ml += tot[j];
+  }
+  const float mass = resid ? Z : wave_sum(ml);
   const float thr = ug * mass;
-  float before;
-  const int cs = owner_select(tot, C, 0.0f, thr, lane, before);
+  // the owner chunk: first chunk whose cumulative mass exceeds thr (chunks
+  // with zero mass never own); rounding guard: the last chunk with mass
+  int cs = -1, last = -1;
+  float before = 0.0f, last_before = 0.0f, base = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const bool in = lane + 64 * j < C;
+    const float t = in ? tot[j] : 0.0f;
+    const float G = base + wave_scan(t, lane);
+    const float Gex = G - t;
+    const uint64_t hit = __ballot(in && t > 0.0f && G > thr);
+    const uint64_t pos = __ballot(in && t > 0.0f);
+    if (cs < 0 && hit) {
+      const int l = __builtin_ctzll(hit);
+      cs = 64 * j + l;
+      before = lane_f(Gex, l);
+    }
+    if (pos) {
+      const int l = 63 - __builtin_clzll(pos);
+      last = 64 * j + l;
+      last_before = lane_f(Gex, l);
+    }
+    base = lane_f(G, 63);
+  }
+  if (cs < 0) {
+    cs = last;
+    before = last_before;
+  }
   if (cs < 0) return row_payload(2, false, 0);   // unreachable for a valid row
-  const float a_s = lane_f(at, cs);
-  const float rho_s = lane_f(rho, cs);
-  const float ct = chunk_offset(lane_f(m1, cs), s);
-  const float cd = chunk_offset(lane_f(m2, cs), s);
-  // sub-chunk sums of the owner chunk, in p units
-  const float* pc = P.part + ((int64_t)r * C + cs) * kPart + (resid ? kPWsub : kPPsub);
-  const float sub = lane < NSUB ? a_s * pc[lane] : 0.0f;
-  float before2;
-  const int ss = owner_select(sub, NSUB, before, thr, lane, before2);
-  if (ss < 0) return row_payload(2, false, 0);
-  // re-read the sub-chunk: 32 lanes x EPV logits, token order lane then element
-  const int su = ss / kHalves, sg = ss - su * kHalves;
-  const int64_t kb = (int64_t)cs * kChunk + (int64_t)su * kThreads * EPV + (int64_t)sg * kHalf * EPV;
-  const int64_t k0 = kb + (int64_t)lane * EPV;
-  float w[EPV];
-  {
-    float lt[EPV], ld[EPV];
-    if (lane < kHalf) {
-      load_group<DT>(P.target, r, P.tstride, k0, P.V, P.t_aligned, lt);
-      if (resid) load_group<DT>(P.draft, rd, P.dstride, k0, P.V, P.d_aligned, ld);
-    }
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      float wv = 0.0f;
-      if (lane < kHalf) {
-        const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(lt[e], s, ct));
-        wv = resid ? resid_w(et, __builtin_amdgcn_exp2f(__builtin_fmaf(ld[e], s, cd)), rho_s) : et;
-      }
-      w[e] = wv;
-    }
+  const int ls = cs & 63, js = cs >> 6;
+  const float a_s = lane_f(pick(at, js), ls);
+  const float rho_s = lane_f(pick(rho, js), ls);
+  const float ct = chunk_offset(lane_f(pick(mt, js), ls), s);
+  const float cd = chunk_offset(lane_f(pick(md, js), ls), s);
+  // p(x), q(x): the logits at x with their chunk's offset and scale
+  float px = 0.0f, qx = 0.0f;
+  if (pair) {
+    const int cx = x / F::CH;
+    const int lxl = cx & 63, jx = cx >> 6;
+    const float mtx = lane_f(pick(mt, jx), lxl), mdx = lane_f(pick(md, jx), lxl);
+    px = chunk_scale(mtx, Mt, St, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(lx, s, chunk_offset(mtx, s)));
+    qx = chunk_scale(mdx, Md, Sd, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(dx, s, chunk_offset(mdx, s)));
   }
-  // running sums in the chunk's units against tau = (thr - before2) / a_s
-  const float tau = (thr - before2) / a_s;
-  float loc[EPV];
-  float run = 0.0f;
-#pragma unroll
-  for (int e = 0; e < EPV; ++e) {
-    run += w[e];
-    loc[e] = run;
+  // re-read the owner chunk and scan its weights in token order
+  const int nb = P.V * F::ESIZE;
+  u32x4 R[2][kU];
+  issue_row<DT, VEC>(row_rsrc(P.target, r, P.tstride_b, nb), cs, lane, R[0]);
+  issue_row<DT, VEC>(row_rsrc(P.draft, resid ? rd : 0, P.dstride_b, resid ? nb : 0), cs, lane, R[1]);
+  float w[F::L], ld[F::L];
+  unpack<DT>(R[0], w);
+  unpack<DT>(R[1], ld);
+  if ((cs + 1) * F::CH > P.V) {
+    mask_tail<DT>(w, cs, P.V, lane);
+    mask_tail<DT>(ld, cs, P.V, lane);
   }
-  const float incl = wave_scan(lane < kHalf ? run : 0.0f, lane);
-  const float excl = incl - (lane < kHalf ? run : 0.0f);
+#pragma unroll
+  for (int k = 0; k < F::L; ++k) {
+    const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(w[k], s, ct));
+    w[k] = resid ? resid_w(et, __builtin_amdgcn_exp2f(__builtin_fmaf(ld[k], s, cd)), rho_s) : et;
+  }
+  // Running sums in the chunk's units against tau = (thr - before) / a_s.
+  // Token order inside the chunk is round u, then lane, then element: a
+  // wave scan of the lane sums per round, rounds in order.
+  const float tau = (thr - before) / a_s;
   int first = 0x7FFFFFFF, lastpos = -1;
-  if (lane < kHalf) {
+  float rbase = 0.0f;
 #pragma unroll
-    for (int e = EPV - 1; e >= 0; --e)
-      if (w[e] > 0.0f && excl + loc[e] > tau) first = lane * EPV + e;
+  for (int u = 0; u < kU; ++u) {
+    float loc[F::EPV];
+    float run = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e)
-      if (w[e] > 0.0f) lastpos = lane * EPV + e;
+    for (int e = 0; e < F::EPV; ++e) {
+      run += w[u * F::EPV + e];
+      loc[e] = run;
+    }
+    const float incl = wave_scan(run, lane);
+    const float excl = rbase + (incl - run);
+    int cand = 0x7FFFFFFF;
+#pragma unroll
+    for (int e = F::EPV - 1; e >= 0; --e) {
+      const int k = u * 64 * F::EPV + lane * F::EPV + e;   // position inside the chunk
+      if (w[u * F::EPV + e] > 0.0f) {
+        if (excl + loc[e] > tau) cand = k;
+        lastpos = max(lastpos, k);
+      }
+    }
+    cand = wave_min_i(cand);
+    if (first == 0x7FFFFFFF) first = cand;   // an earlier round's hit wins
+    rbase = rbase + lane_f(incl, 63);
   }
-  first = wave_min_i(first);
   lastpos = wave_max_i(lastpos);
-  const int pick = first != 0x7FFFFFFF ? first : lastpos;
-  if (pick < 0) return row_payload(2, false, 0);   // unreachable: the sub-chunk has weight > 0
-  const int tok = (int)(kb + pick);
+  const int pickk = first != 0x7FFFFFFF ? first : lastpos;
+  if (pickk < 0) return row_payload(2, false, 0);   // unreachable: the chunk has weight > 0
+  const int tok = cs * F::CH + pickk;
   if (tok >= P.V) return row_payload(2, false, 0);
   bool acc = false;
   if (pair) {
-    const float px = P.rowpart[(int64_t)r * 2 + 0];
-    const float qx = P.rowpart[(int64_t)r * 2 + 1];
     acc = ui * qx < px;
     if (lane == 0) {
       if (P.p_draft) P.p_draft[rd] = px;
@@ -852,37 +1027,37 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
   return row_payload(0, acc, tok);
 }
 
-// One row of a greedy (or invalid-temperature) sequence, on one wave.
-__device__ __forceinline__ uint32_t finish_greedy(const Params& P, int r, int rd, bool pair, bool t_ok,
-                                                  int lane) {
+// One row of a greedy sequence, on one wave.
+template <int NPER>
+__device__ __forceinline__ uint32_t finish_greedy(const Params& P, int r, int rd, bool pair, int lane) {
   const int C = P.C;
   const uint32_t tag = P.epoch;
-  const bool in = lane < C;
+  RowSlots<NPER> q;
+  uint32_t soff[NPER];
+  slot_offsets(C, lane, soff);
+  slots_issue(P, r, true, soff, q);
+  if (!slots_ready(q, C, tag, pair ? 4 : 2, lane)) return row_payload(2, false, 0);
   float av = -__builtin_huge_valf(), dv = -__builtin_huge_valf();
-  int ak = 0x7FFFFFFF, dk = 0x7FFFFFFF, bad = 0, ok = 1;
-  if (in) {
-    const uint64_t* x1 = P.xch1 + ((int64_t)r * C + lane) * kX1;
-    const uint64_t a = __hip_atomic_load(x1 + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t bb = __hip_atomic_load(x1 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t c = __hip_atomic_load(x1 + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t d = __hip_atomic_load(x1 + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ok = ((uint32_t)(a >> 32) == tag) & ((uint32_t)(bb >> 32) == tag) & ((uint32_t)(c >> 32) == tag) &
-         ((uint32_t)(d >> 32) == tag);
-    av = __uint_as_float((uint32_t)a);
-    dv = __uint_as_float((uint32_t)c);
-    bad = ((uint32_t)bb == 0xFFFFFFFFu) || (pair && (uint32_t)d == 0xFFFFFFFFu);
-    ak = (int)(uint32_t)bb;
-    dk = (int)(uint32_t)d;
+  int ak = 0x7FFFFFFF, dk = 0x7FFFFFFF, bad = 0;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    if (lane + 64 * j < C) {
+      argmax_merge(av, ak, slot_f(q.w[j][0]), (int)(uint32_t)q.w[j][1]);
+      bad |= (uint32_t)q.w[j][1] == 0xFFFFFFFFu;
+      if (pair) {
+        argmax_merge(dv, dk, slot_f(q.w[j][2]), (int)(uint32_t)q.w[j][3]);
+        bad |= (uint32_t)q.w[j][3] == 0xFFFFFFFFu;
+      }
+    }
   }
-  if (!__all(ok)) return row_payload(2, false, 0);
   bad = __any(bad);
   wave_argmax(av, ak);
   wave_argmax(dv, dk);
-  if (!t_ok || bad || av == -__builtin_huge_valf() || (pair && dv == -__builtin_huge_valf()))
+  if (bad || av == -__builtin_huge_valf() || (pair && dv == -__builtin_huge_valf()))
     return row_payload(1, false, 0);
   bool acc = false;
   if (pair) {
-    const int x = P.tokens[rd];
+    const int x = ld_const(P.tokens, rd);
     if (x < 0 || x >= P.V) return row_payload(1, false, 0);
     acc = (x == ak);
     if (lane == 0) {
@@ -895,38 +1070,37 @@ __device__ __forceinline__ uint32_t finish_greedy(const Params& P, int r, int rd
   return row_payload(0, acc, ak);
 }
 
-template <int DT>
+template <int DT, bool VEC, int NPER>
 __global__ __launch_bounds__(64 * kFinishWaves) void finish_kernel(Params P) {
   __shared__ FinishShared sh;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
   int d0, gam;
-  bool layout_ok;
   if (P.cu_draft == nullptr) {
     d0 = b * P.gamma;
     gam = P.gamma;
-    layout_ok = true;
   } else {
-    d0 = P.cu_draft[b];
-    gam = P.cu_draft[b + 1] - d0;
-    layout_ok = d0 >= 0 && gam >= 0 && gam <= P.max_gamma && d0 + gam <= P.R_d &&
-                P.cu_draft[0] == 0 && P.cu_draft[P.B] == P.R_d;
-  }
-  if (!layout_ok) {   // the rows of this sequence are unknown: report only
-    if (threadIdx.x == 0) P.acc_len[b] = -1;
-    return;
+    if (*P.layout != P.epoch * 2u) {   // cu_draft is not a layout: every sequence and token is invalid
+      if (threadIdx.x == 0) P.acc_len[b] = -1;
+      for (int t = b + P.B * (int)threadIdx.x; t < P.R_t; t += P.B * (int)blockDim.x) P.out_tokens[t] = -1;
+      return;
+    }
+    d0 = ld_const(P.cu_draft, b);
+    gam = ld_const(P.cu_draft, b + 1) - d0;
   }
   const int t0 = d0 + b;
-  const float T = P.temps[b];
-  const bool t_ok = (T == 0.0f) || (T >= kFltMin && T <= kFltMax);
-  const bool sampled = t_ok && T > 0.0f;
-  const float ug = P.uniforms[t0 + gam];
+  const float T = ld_const(P.temps, b);
+  const bool sampled = t_sampled(T);
+  const bool t_ok = sampled || T == 0.0f;
+  const float ug = ld_const(P.uniforms, t0 + gam);
   for (int j = wv; j <= gam; j += nw) {
     const bool pair = j < gam;
     const int r = t0 + j, rd = d0 + j;
-    const uint32_t res = sampled ? finish_sampled<DT>(P, r, rd, pair, T, P.uniforms[r], ug, lane)
-                                 : finish_greedy(P, r, rd, pair, t_ok, lane);
+    uint32_t res;
+    if (!t_ok) res = row_payload(1, false, 0);
+    else if (sampled) res = finish_sampled<DT, VEC, NPER>(P, r, rd, pair, T, ld_const(P.uniforms, r), ug, lane);
+    else res = finish_greedy<NPER>(P, r, rd, pair, lane);
     if (lane == 0) sh.res[j] = res;
   }
   __syncthreads();
@@ -952,20 +1126,45 @@ __global__ __launch_bounds__(64 * kFinishWaves) void finish_kernel(Params P) {
   if (lane == 0) P.acc_len[b] = st == 2 ? -2 : st == 1 ? -1 : n;
 }
 
-int chunks_for(int V) { return (V + kChunk - 1) / kChunk; }
+// ================================================================== launch table
+
+typedef void (*KernelFn)(Params);
+struct Kernels {
+  KernelFn stream, finish;
+};
+template <int DT, bool VEC>
+Kernels kernels_for(int nper) {
+  if (nper == 1) return {stream_kernel<DT, VEC, 1>, finish_kernel<DT, VEC, 1>};
+  if (nper == 2) return {stream_kernel<DT, VEC, 2>, finish_kernel<DT, VEC, 2>};
+  // more than 128 chunks per row: fp32 only (the bf16 build would not fit
+  // its registers)
+  if constexpr (DT == SPECVERIFY_F32) return {stream_kernel<DT, VEC, 4>, finish_kernel<DT, VEC, 4>};
+  return {nullptr, nullptr};
+}
+Kernels kernels_for(int dtype, bool vec, int nper) {
+  if (dtype == SPECVERIFY_F32) return vec ? kernels_for<SPECVERIFY_F32, true>(nper) : kernels_for<SPECVERIFY_F32, false>(nper);
+  return vec ? kernels_for<SPECVERIFY_BF16, true>(nper) : kernels_for<SPECVERIFY_BF16, false>(nper);
+}
+int chunk_len(int dtype) { return dtype == SPECVERIFY_F32 ? Fmt<SPECVERIFY_F32>::CH : Fmt<SPECVERIFY_BF16>::CH; }
+int chunks_for(int V, int dtype) { return (V + chunk_len(dtype) - 1) / chunk_len(dtype); }
+int max_chunks(int dtype) { return dtype == SPECVERIFY_F32 ? kMaxChunks : kMaxChunksBf16; }
+int nper_for(int C) { return C <= 64 ? 1 : C <= 128 ? 2 : 4; }
 
 }  // namespace
 
 struct specverify_ctx {
   specverify_config cfg;
   int chunks;
+  int nper;
   int64_t rows;            // max target rows
-  int cap;                 // stream workgroups resident at once on the device
+  int cap[2];              // stream workgroups resident at once: [element loads, vector loads]
   void* ws;
   size_t ws_bytes;
   uint64_t* xch1;
+  uint64_t* dummy;
   float* part;
-  float* rowpart;
+  int4* rowinfo;
+  uint32_t* layout;
   uint32_t epoch;
   int timing;              // recording events
   int trec;                // runs recorded since the measurement started
@@ -982,7 +1181,8 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
     return SPECVERIFY_ERR_INVALID_ARGUMENT;
   const int64_t rows = (int64_t)cfg->max_batch * ((int64_t)cfg->max_gamma + 1);
   if (rows > (int64_t)1 << 24) return SPECVERIFY_ERR_INVALID_ARGUMENT;
-  if (chunks_for(cfg->vocab) > kMaxChunks) return SPECVERIFY_ERR_UNSUPPORTED;
+  const int C = chunks_for(cfg->vocab, cfg->dtype);
+  if (C > max_chunks(cfg->dtype)) return SPECVERIFY_ERR_UNSUPPORTED;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev)
     return SPECVERIFY_ERR_DEVICE;
@@ -990,28 +1190,43 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
   if (!h) return SPECVERIFY_ERR_OUT_OF_MEMORY;
   h->cfg = *cfg;
   if (h->cfg.spin_limit == 0) h->cfg.spin_limit = kDefaultSpin;
-  h->chunks = chunks_for(cfg->vocab);
+  if (h->cfg.spin_limit > kMaxSpin) h->cfg.spin_limit = kMaxSpin;
+  h->chunks = C;
+  h->nper = nper_for(C);
   h->rows = rows;
-  const size_t n1 = (size_t)rows * h->chunks * kX1 * sizeof(uint64_t);
-  const size_t n2 = (size_t)rows * h->chunks * kPart * sizeof(float);
-  const size_t n3 = (size_t)rows * 2 * sizeof(float);
-  h->ws_bytes = n1 + n2 + n3;
   int prev = 0;
   (void)hipGetDevice(&prev);
   if (hipSetDevice(cfg->device) != hipSuccess) {
     delete h;
     return SPECVERIFY_ERR_DEVICE;
   }
-  // residency of the persistent stream grid: workgroups per CU times CUs
-  int cus = 0, per_cu = 0;
+  // Residency of the persistent stream grid: workgroups per CU times CUs.
+  // A row group needs at least C waves, so that the chunks of a row fall
+  // into one round or two consecutive ones and their waves meet in time.
+  int cus = 0;
+  h->cap[0] = h->cap[1] = 0;
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cfg->device);
-  if (e == hipSuccess)
-    e = cfg->dtype == SPECVERIFY_F32
-            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_kernel<SPECVERIFY_F32>, kThreads, 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_kernel<SPECVERIFY_BF16>, kThreads, 0);
-  h->cap = (e == hipSuccess) ? cus * per_cu : 0;
+  // A stream kernel that spilled to scratch would make the runtime allocate
+  // scratch at its first launch and spill in its inner loop: such a build is
+  // refused rather than run.
+  for (int v = 0; v < 2 && e == hipSuccess; ++v) {
+    const void* fn = (const void*)kernels_for(cfg->dtype, v == 1, h->nper).stream;
+    int per_cu = 0;
+    hipFuncAttributes fa;
+    e = hipFuncGetAttributes(&fa, fn);
+    if (e == hipSuccess && fa.localSizeBytes > 0) e = hipErrorInvalidConfiguration;
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStreamThreads, 0);
+    h->cap[v] = cus * per_cu;
+    if (e == hipSuccess && (h->cap[v] / kGroups) * kStreamWaves < C) e = hipErrorInvalidConfiguration;
+  }
+  const size_t n1 = (size_t)rows * C * kX1 * sizeof(uint64_t);
+  const int capmax = h->cap[0] > h->cap[1] ? h->cap[0] : h->cap[1];
+  const size_t nd = (size_t)capmax * kStreamWaves * 8 * sizeof(uint64_t);   // dummy slots, per stream wave
+  const size_t n2 = (size_t)rows * C * kPart * sizeof(float);
+  const size_t n3 = (size_t)rows * sizeof(int4);
+  const size_t n4 = 256;                                   // layout flag
+  h->ws_bytes = n1 + nd + n2 + n3 + n4;
   void* p = nullptr;
-  if (e == hipSuccess && h->cap < kGroups) e = hipErrorInvalidConfiguration;
   if (e == hipSuccess) e = hipMalloc(&p, h->ws_bytes);
   if (e == hipSuccess) e = hipMemset(p, 0, h->ws_bytes);   // tag 0 is never an epoch
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -1019,12 +1234,17 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
   if (e != hipSuccess) {
     if (p) (void)hipFree(p);
     delete h;
-    return e == hipErrorOutOfMemory ? SPECVERIFY_ERR_OUT_OF_MEMORY : SPECVERIFY_ERR_DEVICE;
+    return e == hipErrorOutOfMemory ? SPECVERIFY_ERR_OUT_OF_MEMORY
+           : e == hipErrorInvalidConfiguration ? SPECVERIFY_ERR_UNSUPPORTED
+                                               : SPECVERIFY_ERR_DEVICE;
   }
   h->ws = p;
-  h->xch1 = (uint64_t*)p;
-  h->part = (float*)((char*)p + n1);
-  h->rowpart = (float*)((char*)p + n1 + n2);
+  char* q = (char*)p;
+  h->xch1 = (uint64_t*)q;
+  h->dummy = (uint64_t*)(q + n1);
+  h->part = (float*)(q + n1 + nd);
+  h->rowinfo = (int4*)(q + n1 + nd + n2);
+  h->layout = (uint32_t*)(q + n1 + nd + n2 + n3);
   h->epoch = 0;
   h->timing = 0;
   h->trec = 0;
@@ -1058,47 +1278,49 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   const int esize = h->cfg.dtype == SPECVERIFY_F32 ? 4 : 2;
   if (((uintptr_t)in->target_logits % esize) || (R_d > 0 && ((uintptr_t)in->draft_logits % esize)))
     return SPECVERIFY_ERR_UNSUPPORTED;   // logits must be element aligned
-  // Rows that do not start on 16-byte boundaries are read element by element.
-  const bool t_aligned = !((uintptr_t)in->target_logits & 15) && !((in->target_stride * esize) & 15);
-  const bool d_aligned = R_d > 0 && !((uintptr_t)in->draft_logits & 15) && !((in->draft_stride * esize) & 15);
+  // 16-byte loads need rows and the row length on 16-byte boundaries;
+  // otherwise the kernels read element by element.
+  const bool vec = !((uintptr_t)in->target_logits & 15) && !((in->target_stride * esize) & 15) &&
+                   !(((int64_t)V * esize) & 15) &&
+                   (R_d == 0 || (!((uintptr_t)in->draft_logits & 15) && !((in->draft_stride * esize) & 15)));
 
-  // Persistent grid: per row group, as many workgroups as the device holds
-  // (a whole number of rows' worth when it holds that many), never more
-  // than the group has items.
+  // Persistent grid: per row group, as many waves as the device holds, never
+  // more than the busiest group has items.
   const int C = h->chunks;
-  const int64_t rows_g = (R_t + kGroups - 1) / kGroups;
-  int64_t G = h->cap / kGroups;
-  if (G >= C) G = (G / C) * C;
-  if (G > rows_g * C) G = rows_g * C;
-  if (G < 1) G = 1;
+  const int64_t items_g = ((R_t + kGroups - 1) / kGroups) * C;
+  int64_t wg = h->cap[vec ? 1 : 0] / kGroups;
+  const int64_t need = (items_g + kStreamWaves - 1) / kStreamWaves;
+  if (wg > need) wg = need;
+  if (wg < 1) wg = 1;
   const int gmax = in->cu_draft == nullptr ? in->gamma : h->cfg.max_gamma;
   const int fwaves = gmax + 1 < kFinishWaves ? gmax + 1 : kFinishWaves;
 
   if (++h->epoch == 0) h->epoch = 1;   // 0 never tags a slot (workspace is zeroed)
+  if (h->epoch >= 0x80000000u) h->epoch = 1;   // the layout flag holds epoch * 2
   Params P;
-  P.target = in->target_logits;
-  P.draft = in->draft_logits;
-  P.tstride = in->target_stride;
-  P.dstride = in->draft_stride;
+  P.target = (const char*)in->target_logits;
+  P.draft = (const char*)in->draft_logits;
+  P.tstride_b = in->target_stride * esize;
+  P.dstride_b = in->draft_stride * esize;
   P.tokens = in->draft_tokens;
   P.uniforms = in->uniforms;
   P.temps = in->temperatures;
   P.cu_draft = in->cu_draft;
+  P.rowinfo = in->cu_draft ? h->rowinfo : nullptr;
+  P.layout = h->layout;
   P.gamma = in->gamma;
   P.B = B;
   P.R_d = (int32_t)R_d;
   P.R_t = (int32_t)R_t;
   P.V = V;
   P.C = C;
-  P.G = (int32_t)G;
+  P.Gw = (int32_t)(wg * kStreamWaves);
   P.max_gamma = h->cfg.max_gamma;
   P.epoch = h->epoch;
   P.spin_limit = h->cfg.spin_limit;
-  P.t_aligned = t_aligned;
-  P.d_aligned = d_aligned;
   P.xch1 = h->xch1;
+  P.dummy = h->dummy;
   P.part = h->part;
-  P.rowpart = h->rowpart;
   P.acc_len = out->accepted_len;
   P.out_tokens = out->out_tokens;
   P.p_draft = out->p_draft;
@@ -1110,20 +1332,15 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   (void)hipGetDevice(&prev);
   if (prev != h->cfg.device && hipSetDevice(h->cfg.device) != hipSuccess) return SPECVERIFY_ERR_DEVICE;
   hipStream_t stream = (hipStream_t)hip_stream;
-  const dim3 grid((uint32_t)(G * kGroups));
+  const Kernels K = kernels_for(h->cfg.dtype, vec, h->nper);
   hipError_t e = hipSuccess;
   hipEvent_t* ev = nullptr;
   if (h->timing && h->trec < SPECVERIFY_TIMING_RUNS) ev = h->ev + 3 * h->trec++;
   if (ev) e = hipEventRecord(ev[0], stream);
-  if (h->cfg.dtype == SPECVERIFY_F32) {
-    hipLaunchKernelGGL(stream_kernel<SPECVERIFY_F32>, grid, dim3(kThreads), 0, stream, P);
-    if (ev && e == hipSuccess) e = hipEventRecord(ev[1], stream);
-    hipLaunchKernelGGL(finish_kernel<SPECVERIFY_F32>, dim3(B), dim3(64 * fwaves), 0, stream, P);
-  } else {
-    hipLaunchKernelGGL(stream_kernel<SPECVERIFY_BF16>, grid, dim3(kThreads), 0, stream, P);
-    if (ev && e == hipSuccess) e = hipEventRecord(ev[1], stream);
-    hipLaunchKernelGGL(finish_kernel<SPECVERIFY_BF16>, dim3(B), dim3(64 * fwaves), 0, stream, P);
-  }
+  if (in->cu_draft) hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, P, h->rowinfo, h->layout);
+  hipLaunchKernelGGL(K.stream, dim3((uint32_t)(wg * kGroups)), dim3(kStreamThreads), 0, stream, P);
+  if (ev && e == hipSuccess) e = hipEventRecord(ev[1], stream);
+  hipLaunchKernelGGL(K.finish, dim3(B), dim3(64 * fwaves), 0, stream, P);
   if (ev && e == hipSuccess) e = hipEventRecord(ev[2], stream);
   const hipError_t e2 = hipGetLastError();
   if (prev != h->cfg.device) (void)hipSetDevice(prev);

@@ -44,8 +44,10 @@ def test_null_arguments_rejected_without_device():
     assert not h.value
     bad = binding.Config(1, 4, 1000, 7, 0, 0)                      # unknown dtype
     assert lib.specverify_create(ctypes.byref(bad), ctypes.byref(h)) == binding.ERR_INVALID_ARGUMENT
-    bad = binding.Config(1, 4, 524288 + 1, binding.F32, 0, 0)      # more than 64 chunks
-    assert lib.specverify_create(ctypes.byref(bad), ctypes.byref(h)) == binding.ERR_UNSUPPORTED
+    # more than 256 fp32 or 128 bf16 chunks of 4 KB
+    for V, dt in ((262144 + 1, binding.F32), (262144 + 1, binding.BF16)):
+        bad = binding.Config(1, 4, V, dt, 0, 0)
+        assert lib.specverify_create(ctypes.byref(bad), ctypes.byref(h)) == binding.ERR_UNSUPPORTED
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
