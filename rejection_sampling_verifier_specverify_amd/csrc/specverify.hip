@@ -133,6 +133,8 @@ struct Params {
   int32_t max_gamma;
   uint32_t epoch;
   int32_t spin_limit;
+  uint32_t div_c[3];         // unsigned division by C: multiplier and two shifts
+  uint32_t div_g[3];         // unsigned division by gamma + 1 (uniform gamma)
   uint64_t* xch1;            // [rows][C][kX1] tagged slots
   uint64_t* dummy;           // [stream waves][8]: where a wave's step with nothing to publish writes
   float* part;               // [rows][C][kPart]
@@ -270,11 +272,24 @@ __device__ __forceinline__ float chunk_offset(float m, float s) {
 __device__ __forceinline__ float chunk_scale(float m, float M, float S, float s) {
   return __builtin_amdgcn_exp2f((m - M) * s) / S;
 }
-// Weight of one logit pair in the residual, in the chunk's units; the stream
-// and finish kernels compute it with the same operations (built without fp
-// contraction), so the finisher's re-scan sees the stream kernel's bits.
+// rho = a_d / a_t of a chunk (q_k = a_t rho e_d), from the chunk maxima and
+// the row normalisers: 2^(((m_d - M_d) - (m_t - M_t)) s) S_t / S_d.  Both
+// kernels take it from this function, so a chunk's residual weights
+// e_t - min(e_t, rho e_d) have the same bits in both.
+__device__ __forceinline__ float chunk_rho(float mt, float Mt, float St, float md, float Md, float Sd, float s) {
+  return __builtin_amdgcn_exp2f(((md - Md) - (mt - Mt)) * s) * (St * __builtin_amdgcn_rcpf(Sd));
+}
+// min(a, b) of two floats that are >= 0 (+0, positive, +inf or a positive
+// NaN): the unsigned order of their bit patterns is their order, NaN above
+// everything, as fminf treats it.  One integer instruction; fminf would add
+// a canonicalisation of each operand.
+__device__ __forceinline__ float min_nonneg(float a, float b) {
+  return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
+}
+// Weight of one logit pair in the residual, in the chunk's units: e_t minus
+// min(e_t, rho e_d).
 __device__ __forceinline__ float resid_w(float et, float ed, float rho) {
-  return et - fminf(et, rho * ed);
+  return et - min_nonneg(et, rho * ed);
 }
 
 // ------------------------------------------------------------------ chunk slots of a row
@@ -442,6 +457,17 @@ __device__ __forceinline__ T ld_const(const T* p, int64_t i) {
   return ((const __attribute__((address_space(4))) T*)p)[i];
 }
 
+// Unsigned division of n by a run-time constant d with the constants
+// {m, s1, s2} of Granlund and Montgomery ("Division by Invariant Integers
+// using Multiplication", 1994, unsigned case): l = ceil(log2 d),
+// m = floor(2^32 (2^l - d) / d) + 1, s1 = min(l, 1), s2 = max(l - 1, 0);
+// then t = mulhi(m, n) and n / d = (t + ((n - t) >> s1)) >> s2 for every
+// 32-bit n.  Wave-uniform operands make this a few scalar instructions.
+__device__ __forceinline__ uint32_t udiv(uint32_t n, const uint32_t (&k)[3]) {
+  const uint32_t t = __umulhi(k[0], n);
+  return (t + ((n - t) >> k[1])) >> k[2];
+}
+
 struct RowMeta {
   int b;      // sequence (< 0: the batch layout is invalid)
   int rd;     // draft row
@@ -452,7 +478,7 @@ __device__ __forceinline__ RowMeta row_meta(const Params& P, int r) {
   RowMeta m;
   if (P.rowinfo == nullptr) {
     const int g1 = P.gamma + 1;
-    m.b = r / g1;
+    m.b = (int)udiv((uint32_t)r, P.div_g);
     const int i = r - m.b * g1;
     m.pair = i < P.gamma;
     m.rd = m.b * P.gamma + i;
@@ -513,7 +539,7 @@ __device__ __forceinline__ Item make_item(const Params& P, int grp, int idx, int
   it.pair = 0;
   it.s = 0.0f;
   if (idx >= n_items) return it;
-  const int rl = idx / P.C;
+  const int rl = (int)udiv((uint32_t)idx, P.div_c);
   it.c = idx - rl * P.C;
   it.r = grp + kGroups * rl;
   const RowMeta m = row_meta(P, it.r);
@@ -619,7 +645,7 @@ __device__ __forceinline__ void greedy_row(const float (&x)[Fmt<DT>::L], int c, 
 template <int DT>
 __device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lane, uint64_t* wdummy,
                                         const u32x4 (&R)[2][kU], float (&E)[2][Fmt<DT>::L], float& mt,
-                                        float& md) {
+                                        float& md, float& st) {
   unpack<DT>(R[0], E[0]);
   unpack<DT>(R[1], E[1]);
   uint32_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
@@ -631,7 +657,7 @@ __device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lan
       mask_tail<DT>(E[1], it.c, P.V, lane);
     }
     if (it.mode == 1) {
-      float st, sd = 0.0f;
+      float sd = 0.0f;
       md = -__builtin_huge_valf();
       p1_row<DT>(E[0], it.s, mt, st);
       if (it.pair) p1_row<DT>(E[1], it.s, md, sd);
@@ -700,7 +726,7 @@ __device__ __forceinline__ void help_row(const Params& P, const Item& it, int la
 template <int DT, bool VEC, int NPER>
 __device__ __forceinline__ void p2_item(const Params& P, const Item& it, int lane, const uint32_t (&soff)[NPER],
                                         RowSlots<NPER>& q, bool ready,
-                                        const float (&E)[2][Fmt<DT>::L], float mt, float md, float4& o,
+                                        const float (&E)[2][Fmt<DT>::L], float mt, float md, float st, float4& o,
                                         float*& dst) {
   const uint32_t tag = P.epoch;
   if (!ready) {
@@ -722,19 +748,16 @@ __device__ __forceinline__ void p2_item(const Params& P, const Item& it, int lan
   merge_row(q, P.C, 0, it.s, lane, Mt, St);
   merge_row(q, P.C, 2, it.s, lane, Md, Sd);
   // invalid data gives NaN or inf here; the finisher checks the normalisers
-  const float at = chunk_scale(mt, Mt, St, it.s);   // p_k = at e_t
-  const float ad = chunk_scale(md, Md, Sd, it.s);   // q_k = ad e_d
-  const float rho = ad / at;                        // q_k = at rho e_d
-  float w = 0.0f, b = 0.0f;
+  const float rho = chunk_rho(mt, Mt, St, md, Md, Sd, it.s);   // q_k = a_t rho e_d
+  // sum of min(e_t, rho e_d); the residual's sum is the chunk sum of e_t
+  // (phase 1's st, the same values added in the same order) minus it
+  float b = 0.0f;
 #pragma unroll
-  for (int k = 0; k < Fmt<DT>::L; ++k) {
-    const float mn = fminf(E[0][k], rho * E[1][k]);
-    b += mn;
-    w += E[0][k] - mn;
-  }
+  for (int k = 0; k < Fmt<DT>::L; ++k) b += min_nonneg(E[0][k], rho * E[1][k]);
+  const float bs = wave_sum(b);
   o.x = __uint_as_float(tag);
-  o.y = wave_sum(w);
-  o.z = wave_sum(b);
+  o.y = fmaxf(st - bs, 0.0f);
+  o.z = bs;
   dst = P.part + ((int64_t)it.r * P.C + it.c) * kPart;
 }
 
@@ -757,14 +780,14 @@ template <int DT, bool VEC, int NPER>
 __device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy, const uint32_t (&soff)[NPER],
                                      RowSlots<NPER>& q,
                                      const Item& cur, const float (&Ecur)[2][Fmt<DT>::L], float cmt, float cmd,
-                                     const Item& n1, u32x4 (&R1)[2][kU], float (&Efree)[2][Fmt<DT>::L], float& nmt,
-                                     float& nmd, const Item& n3) {
-  p1_item<DT>(P, n1, lane, wdummy, R1, Efree, nmt, nmd);
+                                     float cst, const Item& n1, u32x4 (&R1)[2][kU], float (&Efree)[2][Fmt<DT>::L],
+                                     float& nmt, float& nmd, float& nst, const Item& n3) {
+  p1_item<DT>(P, n1, lane, wdummy, R1, Efree, nmt, nmd, nst);
   if (Poll<NPER>::kLate) slots_issue(P, cur.r, cur.mode == 1 && cur.pair, soff, q);
   const bool ready = slots_ready(q, P.C, P.epoch, kX1, lane);   // consumes the poll on every path
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float* dst = (float*)(wdummy + kX1);
-  if (cur.mode == 1 && cur.pair) p2_item<DT, VEC, NPER>(P, cur, lane, soff, q, ready, Ecur, cmt, cmd, o, dst);
+  if (cur.mode == 1 && cur.pair) p2_item<DT, VEC, NPER>(P, cur, lane, soff, q, ready, Ecur, cmt, cmd, cst, o, dst);
   if (lane == 0) *(float4*)dst = o;
   __builtin_amdgcn_sched_barrier(0);
   if (!Poll<NPER>::kLate) slots_issue(P, n1.r, n1.mode == 1 && n1.pair, soff, q);
@@ -790,7 +813,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void stream_kernel(Params P) {
 
   u32x4 RA[2][kU], RB[2][kU];
   float EA[2][F::L], EB[2][F::L];
-  float amt = 0.0f, amd = 0.0f, bmt = 0.0f, bmd = 0.0f;
+  float amt = 0.0f, amd = 0.0f, ast = 0.0f, bmt = 0.0f, bmd = 0.0f, bst = 0.0f;
   RowSlots<NPER> q;
   // prologue: items 0 and 1 in flight, phase 1 of item 0, its poll, item 2 in flight
   Item ia = make_item(P, grp, j, n_items);
@@ -799,7 +822,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void stream_kernel(Params P) {
   __builtin_amdgcn_sched_barrier(0);
   issue_item<DT, VEC>(P, ib, lane, RB);
   __builtin_amdgcn_sched_barrier(0);
-  p1_item<DT>(P, ia, lane, wdummy, RA, EA, amt, amd);
+  p1_item<DT>(P, ia, lane, wdummy, RA, EA, amt, amd, ast);
   __builtin_amdgcn_sched_barrier(0);
   if (!Poll<NPER>::kLate) slots_issue(P, ia.r, ia.mode == 1 && ia.pair, soff, q);
   __builtin_amdgcn_sched_barrier(0);
@@ -811,10 +834,10 @@ __global__ __launch_bounds__(kStreamThreads, 2) void stream_kernel(Params P) {
   for (int idx = j; idx < n_items; idx += 2 * G) {
     // cur = ia (EA), n1 = ib (RB), n2 = ic (RA, in flight)
     const Item id = make_item(P, grp, idx + 3 * G, n_items);
-    step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ia, EA, amt, amd, ib, RB, EB, bmt, bmd, id);
+    step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ia, EA, amt, amd, ast, ib, RB, EB, bmt, bmd, bst, id);
     // cur = ib (EB), n1 = ic (RA), n2 = id (RB, in flight)
     const Item ie = make_item(P, grp, idx + 4 * G, n_items);
-    step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ib, EB, bmt, bmd, ic, RA, EA, amt, amd, ie);
+    step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ib, EB, bmt, bmd, bst, ic, RA, EA, amt, amd, ast, ie);
     ia = ic;
     ib = id;
     ic = ie;
@@ -899,8 +922,7 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
     mt[j] = in ? slot_f(q.w[j][0]) : ninf;
     md[j] = (in && pair) ? slot_f(q.w[j][2]) : ninf;
     at[j] = in ? chunk_scale(mt[j], Mt, St, s) : 0.0f;
-    const float ad = (in && pair) ? chunk_scale(md[j], Md, Sd, s) : 0.0f;
-    rho[j] = (in && pair) ? ad / at[j] : 0.0f;
+    rho[j] = (in && pair) ? chunk_rho(mt[j], Mt, St, md[j], Md, Sd, s) : 0.0f;
     zl += in ? at[j] * W[j] : 0.0f;
     bl += in ? at[j] * Bp[j] : 0.0f;
   }
@@ -1149,6 +1171,14 @@ int chunk_len(int dtype) { return dtype == SPECVERIFY_F32 ? Fmt<SPECVERIFY_F32>:
 int chunks_for(int V, int dtype) { return (V + chunk_len(dtype) - 1) / chunk_len(dtype); }
 int max_chunks(int dtype) { return dtype == SPECVERIFY_F32 ? kMaxChunks : kMaxChunksBf16; }
 int nper_for(int C) { return C <= 64 ? 1 : C <= 128 ? 2 : 4; }
+// Constants of udiv for the divisor d >= 1.
+void udiv_consts(uint32_t d, uint32_t (&k)[3]) {
+  int l = 0;
+  while (((uint64_t)1 << l) < d) ++l;
+  k[0] = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+  k[1] = l < 1 ? l : 1;
+  k[2] = l > 1 ? l - 1 : 0;
+}
 
 }  // namespace
 
@@ -1318,6 +1348,8 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   P.max_gamma = h->cfg.max_gamma;
   P.epoch = h->epoch;
   P.spin_limit = h->cfg.spin_limit;
+  udiv_consts((uint32_t)C, P.div_c);
+  udiv_consts((uint32_t)(in->cu_draft ? 1 : in->gamma + 1), P.div_g);
   P.xch1 = h->xch1;
   P.dummy = h->dummy;
   P.part = h->part;
