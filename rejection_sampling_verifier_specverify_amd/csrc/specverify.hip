@@ -415,16 +415,23 @@ __device__ __forceinline__ void unpack(const u32x4 (&raw)[kU], float (&x)[Fmt<DT
     }
   }
 }
-// Tokens >= V of the last chunk become -inf.
+// Tokens >= V of the last chunk become -inf, in two rows of the same chunk
+// at once: one comparison per token, and one at a time (each comparison's
+// lane mask is used at once), which keeps the scalar registers of this rare
+// path from crowding the common one.
 template <int DT>
-__device__ __forceinline__ void mask_tail(float (&x)[Fmt<DT>::L], int c, int V, int lane) {
+__device__ __forceinline__ void mask_tail2(float (&x)[Fmt<DT>::L], float (&y)[Fmt<DT>::L], int c, int V, int lane) {
   using F = Fmt<DT>;
-  const int t0 = c * F::CH + lane * F::EPV;
+  const int lim = V - (c * F::CH + lane * F::EPV);
 #pragma unroll
   for (int u = 0; u < kU; ++u)
 #pragma unroll
-    for (int e = 0; e < F::EPV; ++e)
-      if (t0 + u * 64 * F::EPV + e >= V) x[u * F::EPV + e] = -__builtin_huge_valf();
+    for (int e = 0; e < F::EPV; ++e) {
+      const bool out = u * 64 * F::EPV + e >= lim;
+      x[u * F::EPV + e] = out ? -__builtin_huge_valf() : x[u * F::EPV + e];
+      y[u * F::EPV + e] = out ? -__builtin_huge_valf() : y[u * F::EPV + e];
+      __builtin_amdgcn_sched_barrier(0);
+    }
 }
 // Token of element (u, e) of a lane.
 template <int DT>
@@ -433,7 +440,7 @@ __device__ __forceinline__ int token_of(int c, int k, int lane) {
   const int u = k / F::EPV, e = k - u * F::EPV;
   return c * F::CH + u * 64 * F::EPV + lane * F::EPV + e;
 }
-// Element e of vector u of a lane, as unpack and mask_tail leave it; `lim`
+// Element e of vector u of a lane, as unpack and mask_tail2 leave it; `lim`
 // is V minus the token of element 0 of the vector (tokens >= V are -inf).
 template <int DT>
 __device__ __forceinline__ float elem(const u32x4& w, int e, int lim) {
@@ -522,36 +529,40 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(Params P, int4* 
 
 // ================================================================== stream kernel
 
+// An item in three scalar registers: target row (bits 0-23) and chunk (bits
+// 24-31); draft row (bits 0-23), mode (bits 24-25: 0 nothing to do,
+// 1 sampled, 2 greedy) and whether the position has a draft (bit 26);
+// log2(e) / T.  Rows < 2^24 and chunks <= 256 fit.
 struct Item {
-  int r, c;   // target row (< 0: no item), chunk
-  int rd;     // draft row
-  int mode;   // 0 nothing to do, 1 sampled, 2 greedy
-  int pair;   // position has a draft
-  float s;    // log2(e) / T
+  uint32_t rc, rdf;
+  float s;
+  __device__ __forceinline__ int r() const { return (int)(rc & 0xFFFFFFu); }
+  __device__ __forceinline__ int c() const { return (int)(rc >> 24); }
+  __device__ __forceinline__ int rd() const { return (int)(rdf & 0xFFFFFFu); }
+  __device__ __forceinline__ int mode() const { return (int)((rdf >> 24) & 3u); }
+  __device__ __forceinline__ bool pair() const { return (rdf >> 26) & 1u; }
 };
 
 __device__ __forceinline__ Item make_item(const Params& P, int grp, int idx, int n_items) {
   Item it;
-  it.r = -1;
-  it.c = 0;
-  it.rd = 0;
-  it.mode = 0;
-  it.pair = 0;
+  it.rc = 0;
+  it.rdf = 0;
   it.s = 0.0f;
   if (idx >= n_items) return it;
   const int rl = (int)udiv((uint32_t)idx, P.div_c);
-  it.c = idx - rl * P.C;
-  it.r = grp + kGroups * rl;
-  const RowMeta m = row_meta(P, it.r);
+  const int c = idx - rl * P.C;
+  const int r = grp + kGroups * rl;
+  it.rc = (uint32_t)r | ((uint32_t)c << 24);
+  const RowMeta m = row_meta(P, r);
   if (m.b < 0) return it;   // invalid layout: nothing is read
-  it.rd = m.rd;
-  it.pair = m.pair;
+  uint32_t mode = 0;
   if (t_sampled(m.T)) {
-    it.mode = 1;
+    mode = 1;
     it.s = kLog2e / m.T;
   } else if (m.T == 0.0f) {
-    it.mode = 2;
+    mode = 2;
   }   // any other temperature is invalid data: nothing is read
+  it.rdf = (uint32_t)m.rd | (mode << 24) | ((uint32_t)(m.pair != 0) << 26);
   return it;
 }
 
@@ -560,11 +571,11 @@ __device__ __forceinline__ Item make_item(const Params& P, int grp, int idx, int
 template <int DT, bool VEC>
 __device__ __forceinline__ void issue_item(const Params& P, const Item& it, int lane, u32x4 (&R)[2][kU]) {
   const int nb = P.V * Fmt<DT>::ESIZE;
-  const bool live = it.r >= 0 && it.mode != 0;
-  const Rsrc rt = row_rsrc(P.target, live ? it.r : 0, P.tstride_b, live ? nb : 0);
-  const Rsrc rd = row_rsrc(P.draft, (live && it.pair) ? it.rd : 0, P.dstride_b, (live && it.pair) ? nb : 0);
-  issue_row<DT, VEC>(rt, it.c, lane, R[0]);
-  issue_row<DT, VEC>(rd, it.c, lane, R[1]);
+  const bool live = it.mode() != 0;
+  const Rsrc rt = row_rsrc(P.target, live ? it.r() : 0, P.tstride_b, live ? nb : 0);
+  const Rsrc rd = row_rsrc(P.draft, (live && it.pair()) ? it.rd() : 0, P.dstride_b, (live && it.pair()) ? nb : 0);
+  issue_row<DT, VEC>(rt, it.c(), lane, R[0]);
+  issue_row<DT, VEC>(rd, it.c(), lane, R[1]);
 }
 
 // Phase 1 of a sampled row: chunk max, exponentials in place, chunk sum.
@@ -650,17 +661,14 @@ __device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lan
   unpack<DT>(R[1], E[1]);
   uint32_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
   uint64_t* dst = wdummy;
-  if (it.mode != 0) {
-    dst = P.xch1 + ((int64_t)it.r * P.C + it.c) * kX1;
-    if ((it.c + 1) * Fmt<DT>::CH > P.V) {
-      mask_tail<DT>(E[0], it.c, P.V, lane);
-      mask_tail<DT>(E[1], it.c, P.V, lane);
-    }
-    if (it.mode == 1) {
+  if (it.mode() != 0) {
+    dst = P.xch1 + ((int64_t)it.r() * P.C + it.c()) * kX1;
+    if ((it.c() + 1) * Fmt<DT>::CH > P.V) mask_tail2<DT>(E[0], E[1], it.c(), P.V, lane);
+    if (it.mode() == 1) {
       float sd = 0.0f;
       md = -__builtin_huge_valf();
       p1_row<DT>(E[0], it.s, mt, st);
-      if (it.pair) p1_row<DT>(E[1], it.s, md, sd);
+      if (it.pair()) p1_row<DT>(E[1], it.s, md, sd);
       v0 = __float_as_uint(mt);
       v1 = __float_as_uint(st);
       v2 = __float_as_uint(md);
@@ -668,8 +676,8 @@ __device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lan
     } else {
       float vt, vd = -__builtin_huge_valf();
       int kt, kd = 0x7FFFFFFF, bt, bd = 0;
-      greedy_row<DT>(E[0], it.c, lane, vt, kt, bt);
-      if (it.pair) greedy_row<DT>(E[1], it.c, lane, vd, kd, bd);
+      greedy_row<DT>(E[0], it.c(), lane, vt, kt, bt);
+      if (it.pair()) greedy_row<DT>(E[1], it.c(), lane, vd, kd, bd);
       v0 = __float_as_uint(vt);
       v1 = bt ? 0xFFFFFFFFu : (uint32_t)kt;
       v2 = __float_as_uint(vd);
@@ -701,8 +709,8 @@ __device__ __forceinline__ void help_row(const Params& P, const Item& it, int la
     miss[j] = __ballot(m);
   }
   const int nb = P.V * Fmt<DT>::ESIZE;
-  const Rsrc rt = row_rsrc(P.target, it.r, P.tstride_b, nb);
-  const Rsrc rd = row_rsrc(P.draft, it.rd, P.dstride_b, nb);
+  const Rsrc rt = row_rsrc(P.target, it.r(), P.tstride_b, nb);
+  const Rsrc rd = row_rsrc(P.draft, it.rd(), P.dstride_b, nb);
 #pragma unroll
   for (int j = 0; j < NPER; ++j) {
     uint64_t mask = miss[j];
@@ -714,7 +722,7 @@ __device__ __forceinline__ void help_row(const Params& P, const Item& it, int la
       stats_mem<DT, VEC>(rd, c, P.V, lane, it.s, md, sd);
       if (lane < kX1) {
         const uint32_t x = __float_as_uint(lane == 0 ? mt : lane == 1 ? st : lane == 2 ? md : sd);
-        slot_put(P.xch1 + ((int64_t)it.r * P.C + c) * kX1 + lane, tag, x);
+        slot_put(P.xch1 + ((int64_t)it.r() * P.C + c) * kX1 + lane, tag, x);
       }
     }
   }
@@ -740,7 +748,7 @@ __device__ __forceinline__ void p2_item(const Params& P, const Item& it, int lan
         __builtin_amdgcn_s_sleep(2);
       }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the loads below are read again on every turn
-      slots_issue(P, it.r, true, soff, q);
+      slots_issue(P, it.r(), true, soff, q);
       if (slots_ready(q, P.C, tag, kX1, lane)) break;
     }
   }
@@ -758,7 +766,7 @@ __device__ __forceinline__ void p2_item(const Params& P, const Item& it, int lan
   o.x = __uint_as_float(tag);
   o.y = fmaxf(st - bs, 0.0f);
   o.z = bs;
-  dst = P.part + ((int64_t)it.r * P.C + it.c) * kPart;
+  dst = P.part + ((int64_t)it.r() * P.C + it.c()) * kPart;
 }
 
 // One pipeline step, with the slots of `cur`'s row already in flight in q:
@@ -783,14 +791,14 @@ __device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy
                                      float cst, const Item& n1, u32x4 (&R1)[2][kU], float (&Efree)[2][Fmt<DT>::L],
                                      float& nmt, float& nmd, float& nst, const Item& n3) {
   p1_item<DT>(P, n1, lane, wdummy, R1, Efree, nmt, nmd, nst);
-  if (Poll<NPER>::kLate) slots_issue(P, cur.r, cur.mode == 1 && cur.pair, soff, q);
+  if (Poll<NPER>::kLate) slots_issue(P, cur.r(), cur.mode() == 1 && cur.pair(), soff, q);
   const bool ready = slots_ready(q, P.C, P.epoch, kX1, lane);   // consumes the poll on every path
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float* dst = (float*)(wdummy + kX1);
-  if (cur.mode == 1 && cur.pair) p2_item<DT, VEC, NPER>(P, cur, lane, soff, q, ready, Ecur, cmt, cmd, cst, o, dst);
+  if (cur.mode() == 1 && cur.pair()) p2_item<DT, VEC, NPER>(P, cur, lane, soff, q, ready, Ecur, cmt, cmd, cst, o, dst);
   if (lane == 0) *(float4*)dst = o;
   __builtin_amdgcn_sched_barrier(0);
-  if (!Poll<NPER>::kLate) slots_issue(P, n1.r, n1.mode == 1 && n1.pair, soff, q);
+  if (!Poll<NPER>::kLate) slots_issue(P, n1.r(), n1.mode() == 1 && n1.pair(), soff, q);
   __builtin_amdgcn_sched_barrier(0);
   issue_item<DT, VEC>(P, n3, lane, R1);
   __builtin_amdgcn_sched_barrier(0);
@@ -824,7 +832,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void stream_kernel(Params P) {
   __builtin_amdgcn_sched_barrier(0);
   p1_item<DT>(P, ia, lane, wdummy, RA, EA, amt, amd, ast);
   __builtin_amdgcn_sched_barrier(0);
-  if (!Poll<NPER>::kLate) slots_issue(P, ia.r, ia.mode == 1 && ia.pair, soff, q);
+  if (!Poll<NPER>::kLate) slots_issue(P, ia.r(), ia.mode() == 1 && ia.pair(), soff, q);
   __builtin_amdgcn_sched_barrier(0);
   Item ic = make_item(P, grp, j + 2 * G, n_items);
   issue_item<DT, VEC>(P, ic, lane, RA);
@@ -992,10 +1000,7 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
   float w[F::L], ld[F::L];
   unpack<DT>(R[0], w);
   unpack<DT>(R[1], ld);
-  if ((cs + 1) * F::CH > P.V) {
-    mask_tail<DT>(w, cs, P.V, lane);
-    mask_tail<DT>(ld, cs, P.V, lane);
-  }
+  if ((cs + 1) * F::CH > P.V) mask_tail2<DT>(w, ld, cs, P.V, lane);
 #pragma unroll
   for (int k = 0; k < F::L; ++k) {
     const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(w[k], s, ct));
