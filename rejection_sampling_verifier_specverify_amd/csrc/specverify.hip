@@ -939,6 +939,23 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
     Z = wave_sum(zl);
     beta = wave_sum(bl);
   }
+  // p(x), q(x): the logits at x with their chunk's offset and scale; the
+  // acceptance test u q(x) < p(x)
+  if (pair) {
+    const int cx = x / F::CH;
+    const int lxl = cx & 63, jx = cx >> 6;
+    const float mtx = lane_f(pick(mt, jx), lxl), mdx = lane_f(pick(md, jx), lxl);
+    const float px = chunk_scale(mtx, Mt, St, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(lx, s, chunk_offset(mtx, s)));
+    const float qx = chunk_scale(mdx, Md, Sd, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(dx, s, chunk_offset(mdx, s)));
+    if (lane == 0) {
+      if (P.p_draft) P.p_draft[rd] = px;
+      if (P.q_draft) P.q_draft[rd] = qx;
+      if (P.beta) P.beta[rd] = beta;
+      if (P.resid) P.resid[rd] = Z;
+    }
+    // an accepted draft emits itself: its row's residual token is never used
+    if (ui * qx < px) return row_payload(0, true, 0);
+  }
   const bool resid = pair && Z > 0.0f;
   float ml = 0.0f;
 #pragma unroll
@@ -983,15 +1000,6 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
   const float rho_s = lane_f(pick(rho, js), ls);
   const float ct = chunk_offset(lane_f(pick(mt, js), ls), s);
   const float cd = chunk_offset(lane_f(pick(md, js), ls), s);
-  // p(x), q(x): the logits at x with their chunk's offset and scale
-  float px = 0.0f, qx = 0.0f;
-  if (pair) {
-    const int cx = x / F::CH;
-    const int lxl = cx & 63, jx = cx >> 6;
-    const float mtx = lane_f(pick(mt, jx), lxl), mdx = lane_f(pick(md, jx), lxl);
-    px = chunk_scale(mtx, Mt, St, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(lx, s, chunk_offset(mtx, s)));
-    qx = chunk_scale(mdx, Md, Sd, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(dx, s, chunk_offset(mdx, s)));
-  }
   // re-read the owner chunk and scan its weights in token order
   const int nb = P.V * F::ESIZE;
   u32x4 R[2][kU];
@@ -1041,17 +1049,7 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
   if (pickk < 0) return row_payload(2, false, 0);   // unreachable: the chunk has weight > 0
   const int tok = cs * F::CH + pickk;
   if (tok >= P.V) return row_payload(2, false, 0);
-  bool acc = false;
-  if (pair) {
-    acc = ui * qx < px;
-    if (lane == 0) {
-      if (P.p_draft) P.p_draft[rd] = px;
-      if (P.q_draft) P.q_draft[rd] = qx;
-      if (P.beta) P.beta[rd] = beta;
-      if (P.resid) P.resid[rd] = Z;
-    }
-  }
-  return row_payload(0, acc, tok);
+  return row_payload(0, false, tok);
 }
 
 // One row of a greedy sequence, on one wave.
