@@ -32,13 +32,11 @@
 //             min(p, q) = a_t min(e_t, rho e_d) and max(0, p - q) =
 //             a_t (e_t - min(e_t, rho e_d)); the chunk sums of both (beta,
 //             velog section 2-3 item 1; residual mass Z, item 2) go out.
-// The waves are software pipelined: while the slots of item k's row are in
-// flight, the wave runs phase 1 of item k + 1, and the 16-byte loads of
-// item k + 2 are in flight behind both.  The poll of item k's slots is
-// issued before the loads of item k + 2, so waiting for it never waits for
-// them.  Logits are read with buffer loads: a row without a draft gets a
-// zero-sized buffer, so every item issues the same loads and none of them
-// touches memory it should not.
+// The waves are software pipelined: a step runs phase 1 of item k + 1, then
+// polls item k's row and runs its phase 2, with the 16-byte loads of items
+// k + 2 and k + 3 in flight.  Logits are read with buffer loads: a row
+// without a draft gets a zero-sized buffer, so every item issues the same
+// loads and none of them touches memory it should not.
 //
 // finish_kernel, one workgroup per sequence and one wave per row, then
 // merges the partials: Z and beta; p(x) and q(x) from the two logits of the
@@ -769,21 +767,19 @@ __device__ __forceinline__ void p2_item(const Params& P, const Item& it, int lan
   dst = P.part + ((int64_t)it.r() * P.C + it.c()) * kPart;
 }
 
-// One pipeline step, with the slots of `cur`'s row already in flight in q:
+// One pipeline step:
 //   phase 1 of n1 (its loads were issued two steps ago; exponentials into
-//   Efree), phase 2 of cur (exponentials in Ecur), then the poll of n1's
-//   row, then the loads of n3 into n1's buffer, now free.
-// The poll goes out before the loads: vector memory operations complete in
-// order, so waiting for the poll in the next step never waits for them.
+//   Efree), then the poll of cur's row, phase 2 of cur (exponentials in
+//   Ecur), then the loads of n3 into n1's buffer, now free.
+// The poll goes out after phase 1 of n1, a whole phase after cur's own
+// phase 1, so that the other chunks of its row have mostly published by
+// then.  Vector memory operations complete in order, so waiting for it also
+// waits for n2's loads, issued a step earlier: those are needed next step
+// anyway.  (Issuing the poll a step earlier, before n3's loads, measured
+// 1 us slower per launch: it more often found the row incomplete.)
 // Every path through a step issues the same memory operations (items that
 // do not exist read zero-sized buffers and write the dummy slots), so the
 // compiler's count of operations in flight is exact at every wait.
-// With more than 128 chunks per row the slots of a row take too many
-// registers to keep across phase 1: the poll is issued after it instead.
-template <int NPER>
-struct Poll {
-  static constexpr bool kLate = NPER > 2;
-};
 template <int DT, bool VEC, int NPER>
 __device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy, const uint32_t (&soff)[NPER],
                                      RowSlots<NPER>& q,
@@ -791,14 +787,12 @@ __device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy
                                      float cst, const Item& n1, u32x4 (&R1)[2][kU], float (&Efree)[2][Fmt<DT>::L],
                                      float& nmt, float& nmd, float& nst, const Item& n3) {
   p1_item<DT>(P, n1, lane, wdummy, R1, Efree, nmt, nmd, nst);
-  if (Poll<NPER>::kLate) slots_issue(P, cur.r(), cur.mode() == 1 && cur.pair(), soff, q);
+  slots_issue(P, cur.r(), cur.mode() == 1 && cur.pair(), soff, q);
   const bool ready = slots_ready(q, P.C, P.epoch, kX1, lane);   // consumes the poll on every path
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float* dst = (float*)(wdummy + kX1);
   if (cur.mode() == 1 && cur.pair()) p2_item<DT, VEC, NPER>(P, cur, lane, soff, q, ready, Ecur, cmt, cmd, cst, o, dst);
   if (lane == 0) *(float4*)dst = o;
-  __builtin_amdgcn_sched_barrier(0);
-  if (!Poll<NPER>::kLate) slots_issue(P, n1.r(), n1.mode() == 1 && n1.pair(), soff, q);
   __builtin_amdgcn_sched_barrier(0);
   issue_item<DT, VEC>(P, n3, lane, R1);
   __builtin_amdgcn_sched_barrier(0);
@@ -823,7 +817,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void stream_kernel(Params P) {
   float EA[2][F::L], EB[2][F::L];
   float amt = 0.0f, amd = 0.0f, ast = 0.0f, bmt = 0.0f, bmd = 0.0f, bst = 0.0f;
   RowSlots<NPER> q;
-  // prologue: items 0 and 1 in flight, phase 1 of item 0, its poll, item 2 in flight
+  // prologue: items 0 and 1 in flight, phase 1 of item 0, item 2 in flight
   Item ia = make_item(P, grp, j, n_items);
   Item ib = make_item(P, grp, j + G, n_items);
   issue_item<DT, VEC>(P, ia, lane, RA);
@@ -831,8 +825,6 @@ __global__ __launch_bounds__(kStreamThreads, 2) void stream_kernel(Params P) {
   issue_item<DT, VEC>(P, ib, lane, RB);
   __builtin_amdgcn_sched_barrier(0);
   p1_item<DT>(P, ia, lane, wdummy, RA, EA, amt, amd, ast);
-  __builtin_amdgcn_sched_barrier(0);
-  if (!Poll<NPER>::kLate) slots_issue(P, ia.r(), ia.mode() == 1 && ia.pair(), soff, q);
   __builtin_amdgcn_sched_barrier(0);
   Item ic = make_item(P, grp, j + 2 * G, n_items);
   issue_item<DT, VEC>(P, ic, lane, RA);
