@@ -4,3 +4,4 @@ Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` import this package; the product path never does.
 """
 from .specverify_oracle import *  # noqa: F401,F403
+from .commit_oracle import commit_reference  # noqa: F401
