@@ -183,6 +183,21 @@ def cpu_baseline(inp, budget_s: float):
                        f"one process, one thread")
 
 
+def cpu_commit_baseline(inp, out, cap) -> float:
+    """The commit oracle on the host, one thread, over the same run outputs:
+    microseconds per call (about 1 s of calls)."""
+    from oracle import commit_reference
+    acc = out["accepted_len"].cpu().numpy()
+    toks = out["out_tokens"].cpu().numpy()
+    rows = np.zeros((inp.batch, cap), dtype=np.int32)
+    lens = np.zeros(inp.batch, dtype=np.int32)
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        commit_reference(acc, toks, inp.cu_draft, rows, lens, cap)
+        n += 1
+    return (time.perf_counter() - t0) / n * 1e6
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -258,6 +273,31 @@ def main():
     stream_ms = ks / nrec
     finish_ms = kf / nrec
 
+    # The on-device commit of a step (specverify_commit): K commits of the last
+    # step's outputs into token rows with room for all of them, between two
+    # events on the launch stream.
+    cap = args.steps * (int(inp.gammas.max()) + 1) + 1
+    seq_tokens = torch.zeros((B, cap), dtype=torch.int32, device=dev)
+    seq_lens = torch.zeros(B, dtype=torch.int32, device=dev)
+    appended = torch.empty(B, dtype=torch.int32, device=dev)
+    next_token = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def commit():
+        sv.commit(out["accepted_len"], out["out_tokens"], seq_tokens, seq_lens, appended=appended,
+                  next_token=next_token, **gamma_kw)
+
+    for _ in range(5):
+        commit()
+    seq_lens.zero_()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        commit()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    commit_us = ev0.elapsed_time(ev1) / args.steps * 1e3
+    assert int(seq_lens.min()) >= args.steps   # every call appended to every sequence
+
     if args.copy_probe:   # plain copy of the logits' size, for FETCH/WRITE_SIZE calibration
         src = torch.empty(logit_bytes // 2, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)
@@ -294,9 +334,15 @@ def main():
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic, "kernel": "stream_kernel",
                      "alg_bytes_per_launch": logit_bytes, "kernel_launches_timed": nrec},
         "step_GBps": alg_bytes / (ms * 1e-3) / 1e9,
+        "commit": {"kernel": "commit_kernel", "us_per_call": commit_us, "sequences": B,
+                   # reads accepted_len, out_tokens, seq_lens; writes at most R_t tokens
+                   # and seq_lens, appended, next_token
+                   "bytes_per_call_max": 4 * (2 * R_t + 5 * B),
+                   "bound": "latency"},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        res["commit"]["cpu_oracle_us_per_call"] = cpu_commit_baseline(inp, out, cap)
     sv.close()
     print(json.dumps(res), flush=True)
 

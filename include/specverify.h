@@ -134,6 +134,44 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
 specverify_status specverify_run(specverify_handle h, const specverify_inputs* in,
                                  const specverify_outputs* out, void* hip_stream);
 
+/* On-device commit of a verification step (Perplexity "Accelerating Sonar
+ * through speculation", section "단일 토큰에 대한 MTP 스케줄링": after the drafts
+ * are verified, a kernel places the next target token after the target's
+ * shifted input tokens, so the accepted length never has to reach the host).
+ * For every sequence b with 0 <= n_b = accepted_len[b] <= gamma_b, the
+ * n_b + 1 emitted tokens out_tokens[cu_t[b] .. cu_t[b] + n_b] are appended to
+ * row b of seq_tokens at seq_lens[b]; seq_lens[b] grows by n_b + 1,
+ * appended[b] = n_b + 1 and next_token[b] = out_tokens[cu_t[b] + n_b] (the
+ * token that starts b's next step).  A sequence with n_b < 0 (invalid) or
+ * n_b > gamma_b, or whose layout lies outside the R_d draft rows, is left
+ * unchanged with appended[b] = 0; one whose tokens do not fit (seq_lens[b]
+ * < 0 or seq_lens[b] + n_b + 1 > capacity) is left unchanged with
+ * appended[b] = -1; both get next_token[b] = -1.  The layout is the run's:
+ * cu_t[b] = cu_draft[b] + b, or b * (gamma + 1) when cu_draft is NULL.
+ * Every pointer is device memory; the call is asynchronous on hip_stream and
+ * must be ordered after the run whose outputs it reads. */
+typedef struct {
+  int32_t batch;                /* B <= max_batch (0 = nothing to do)                 */
+  int32_t gamma;                /* uniform draft length, used iff cu_draft == NULL    */
+  const int32_t* cu_draft;      /* [B+1] draft-row offsets of the run, or NULL        */
+  int32_t num_draft_rows;       /* R_d = cu_draft[B] (host copy), used iff cu_draft   */
+  const int32_t* accepted_len;  /* [B] from specverify_run                            */
+  const int32_t* out_tokens;    /* [R_t] from specverify_run                          */
+  int32_t* seq_tokens;          /* [B, seq_stride] committed tokens, in/out           */
+  int64_t seq_stride;           /* elements between rows, >= capacity                 */
+  int32_t capacity;             /* tokens a row may hold                              */
+  int32_t* seq_lens;            /* [B] committed lengths, in/out                      */
+  int32_t* appended;            /* [B] out: n_b + 1, 0 or -1 as above; or NULL        */
+  int32_t* next_token;          /* [B] out, or NULL                                   */
+} specverify_commit_args;
+
+/* Errors (no launch happens): INVALID_ARGUMENT for a NULL handle, args or
+ * required pointer, B > max_batch, gamma outside [0, max_gamma], R_t above
+ * the handle's rows, capacity < 0 or seq_stride < capacity; DEVICE if the
+ * launch fails. */
+specverify_status specverify_commit(specverify_handle h, const specverify_commit_args* a,
+                                    void* hip_stream);
+
 /* Free the workspace and the handle (NULL is accepted). */
 specverify_status specverify_destroy(specverify_handle h);
 

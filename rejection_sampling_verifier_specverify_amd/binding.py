@@ -24,7 +24,7 @@ CHUNK = {"bf16": 2048, "f32": 1024}   # logits per V-chunk (4 KB of a row: one w
 MAX_CHUNKS = {"bf16": 128, "f32": 256}
 EXPORTED = ("specverify_create", "specverify_run", "specverify_destroy",
             "specverify_set_timing", "specverify_timing_totals",
-            "specverify_chunks_per_row", "specverify_workspace_bytes")
+            "specverify_chunks_per_row", "specverify_workspace_bytes", "specverify_commit")
 
 
 class Config(ctypes.Structure):
@@ -46,6 +46,15 @@ class Outputs(ctypes.Structure):
     _fields_ = [("accepted_len", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
                 ("p_draft", ctypes.c_void_p), ("q_draft", ctypes.c_void_p),
                 ("beta", ctypes.c_void_p), ("resid_mass", ctypes.c_void_p)]
+
+
+class CommitArgs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("gamma", ctypes.c_int32),
+                ("cu_draft", ctypes.c_void_p), ("num_draft_rows", ctypes.c_int32),
+                ("accepted_len", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
+                ("seq_tokens", ctypes.c_void_p), ("seq_stride", ctypes.c_int64),
+                ("capacity", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
+                ("appended", ctypes.c_void_p), ("next_token", ctypes.c_void_p)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -91,6 +100,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                              ctypes.POINTER(ctypes.c_float),
                                              ctypes.POINTER(ctypes.c_float)]
     lib.specverify_timing_totals.restype = ctypes.c_int
+    lib.specverify_commit.argtypes = [ctypes.c_void_p, ctypes.POINTER(CommitArgs), ctypes.c_void_p]
+    lib.specverify_commit.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -108,6 +119,12 @@ def specverify_run(h: ctypes.c_void_p, inputs: Inputs, outputs: Outputs, stream:
                                        ctypes.c_void_p(stream))
     if st != OK:
         raise SpecVerifyError("specverify_run", st)
+
+
+def specverify_commit(h: ctypes.c_void_p, args: CommitArgs, stream: int) -> None:
+    st = load_library().specverify_commit(h, ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != OK:
+        raise SpecVerifyError("specverify_commit", st)
 
 
 def specverify_destroy(h: ctypes.c_void_p) -> None:
@@ -201,3 +218,33 @@ class SpecVerify:
                       _ptr(beta), _ptr(resid_mass))
         s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
         specverify_run(self.handle, inp, out, int(s))
+
+    def commit(self, accepted_len, out_tokens, seq_tokens, seq_lens, *, gamma: Optional[int] = None,
+               cu_draft=None, num_draft_rows: Optional[int] = None, appended=None, next_token=None,
+               stream=None) -> None:
+        """Append each sequence's emitted tokens of a run to its row of
+        ``seq_tokens`` [B, capacity] (int32, device) at ``seq_lens`` [B]; see
+        specverify_commit in include/specverify.h."""
+        import torch
+        if seq_tokens.dim() != 2 or seq_tokens.stride(1) != 1:
+            raise ValueError("seq_tokens must be a 2-D tensor with unit column stride")
+        a = CommitArgs()
+        a.batch = int(accepted_len.shape[0])
+        if cu_draft is None:
+            a.gamma = int(gamma)
+            a.cu_draft = None
+            a.num_draft_rows = a.batch * int(gamma)
+        else:
+            a.gamma = 0
+            a.cu_draft = _ptr(cu_draft)
+            a.num_draft_rows = int(num_draft_rows)
+        a.accepted_len = _ptr(accepted_len)
+        a.out_tokens = _ptr(out_tokens)
+        a.seq_tokens = _ptr(seq_tokens)
+        a.seq_stride = int(seq_tokens.stride(0))
+        a.capacity = int(seq_tokens.shape[1])
+        a.seq_lens = _ptr(seq_lens)
+        a.appended = _ptr(appended)
+        a.next_token = _ptr(next_token)
+        s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
+        specverify_commit(self.handle, a, int(s))

@@ -1143,6 +1143,54 @@ __global__ __launch_bounds__(64 * kFinishWaves) void finish_kernel(Params P) {
   if (lane == 0) P.acc_len[b] = st == 2 ? -2 : st == 1 ? -1 : n;
 }
 
+// ================================================================== commit kernel
+
+// The commit of a verification step (see specverify_commit in the header):
+// one wave per sequence appends its n + 1 emitted tokens to its token row.
+struct CommitParams {
+  int32_t B, gamma, R_d, capacity;
+  const int32_t* cu_draft;   // NULL: uniform gamma
+  const int32_t* acc_len;
+  const int32_t* out_tokens;
+  int32_t* seq_tokens;
+  int64_t seq_stride;
+  int32_t* seq_lens;
+  int32_t* appended;         // may be NULL
+  int32_t* next_token;       // may be NULL
+};
+constexpr int kCommitWaves = 4;
+
+__global__ __launch_bounds__(64 * kCommitWaves) void commit_kernel(CommitParams C) {
+  const int lane = threadIdx.x & 63;
+  const int b = (int)blockIdx.x * kCommitWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (b >= C.B) return;
+  int d0, gam;
+  if (C.cu_draft == nullptr) {
+    d0 = b * C.gamma;
+    gam = C.gamma;
+  } else {
+    d0 = ld_const(C.cu_draft, b);
+    gam = ld_const(C.cu_draft, b + 1) - d0;
+  }
+  const int n = ld_const(C.acc_len, b);
+  // a length the layout does not allow, or a layout outside the run's rows,
+  // counts as an invalid sequence: nothing outside the buffers is read
+  const bool valid = n >= 0 && n <= gam && d0 >= 0 && d0 + gam <= C.R_d;
+  const int k = n + 1;
+  const int start = ld_const(C.seq_lens, b);
+  const bool fits = valid && start >= 0 && start <= C.capacity - k;
+  const int t0 = d0 + b;   // first target row of the sequence
+  if (fits) {
+    int32_t* row = C.seq_tokens + (int64_t)b * C.seq_stride + start;
+    for (int j = lane; j < k; j += 64) row[j] = C.out_tokens[t0 + j];
+  }
+  if (lane == 0) {
+    if (fits) C.seq_lens[b] = start + k;
+    if (C.appended) C.appended[b] = fits ? k : valid ? -1 : 0;
+    if (C.next_token) C.next_token[b] = fits ? C.out_tokens[t0 + n] : -1;
+  }
+}
+
 // ================================================================== launch table
 
 typedef void (*KernelFn)(Params);
@@ -1372,6 +1420,46 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   const hipError_t e2 = hipGetLastError();
   if (prev != h->cfg.device) (void)hipSetDevice(prev);
   return (e == hipSuccess && e2 == hipSuccess) ? SPECVERIFY_OK : SPECVERIFY_ERR_DEVICE;
+}
+
+specverify_status specverify_commit(specverify_handle h, const specverify_commit_args* a, void* hip_stream) {
+  if (!h || !a) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  const int B = a->batch;
+  if (B < 0 || B > h->cfg.max_batch) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  if (B == 0) return SPECVERIFY_OK;
+  int64_t R_d;
+  if (a->cu_draft == nullptr) {
+    if (a->gamma < 0 || a->gamma > h->cfg.max_gamma) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+    R_d = (int64_t)B * a->gamma;
+  } else {
+    if (a->num_draft_rows < 0) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+    R_d = a->num_draft_rows;
+  }
+  if (R_d + B > h->rows) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  if (!a->accepted_len || !a->out_tokens || !a->seq_tokens || !a->seq_lens || a->capacity < 0 ||
+      a->seq_stride < a->capacity)
+    return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  CommitParams C;
+  C.B = B;
+  C.gamma = a->cu_draft ? 0 : a->gamma;
+  C.R_d = (int32_t)R_d;
+  C.capacity = a->capacity;
+  C.cu_draft = a->cu_draft;
+  C.acc_len = a->accepted_len;
+  C.out_tokens = a->out_tokens;
+  C.seq_tokens = a->seq_tokens;
+  C.seq_stride = a->seq_stride;
+  C.seq_lens = a->seq_lens;
+  C.appended = a->appended;
+  C.next_token = a->next_token;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  if (prev != h->cfg.device && hipSetDevice(h->cfg.device) != hipSuccess) return SPECVERIFY_ERR_DEVICE;
+  hipLaunchKernelGGL(commit_kernel, dim3((uint32_t)((B + kCommitWaves - 1) / kCommitWaves)),
+                     dim3(64 * kCommitWaves), 0, (hipStream_t)hip_stream, C);
+  const hipError_t e = hipGetLastError();
+  if (prev != h->cfg.device) (void)hipSetDevice(prev);
+  return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_ERR_DEVICE;
 }
 
 specverify_status specverify_destroy(specverify_handle h) {

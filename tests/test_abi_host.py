@@ -30,11 +30,13 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(binding.Config) == 24
     assert ctypes.sizeof(binding.Inputs) == 8 + 8 + 8 + 8 + 8 + 8 + 8 + 8 + 8 + 8
     assert ctypes.sizeof(binding.Outputs) == 48
+    assert ctypes.sizeof(binding.CommitArgs) == 88
 
 
 def test_null_arguments_rejected_without_device():
     lib = binding.load_library()
     assert lib.specverify_run(None, None, None, None) == binding.ERR_INVALID_ARGUMENT
+    assert lib.specverify_commit(None, None, None) == binding.ERR_INVALID_ARGUMENT
     assert lib.specverify_destroy(None) == binding.OK
     assert lib.specverify_chunks_per_row(None) == 0
     h = ctypes.c_void_p()

@@ -1,0 +1,143 @@
+"""GPU parity of the on-device commit (specverify_commit) against its oracle
+(oracle/commit_oracle.py): every output compared exactly, on random
+layouts with invalid and overflowing sequences, and chained after real
+verification runs."""
+import numpy as np
+import pytest
+
+from oracle import commit_reference
+from rejection_sampling_verifier_specverify_amd.binding import SpecVerify, SpecVerifyError
+from rejection_sampling_verifier_specverify_amd.workloads import make_inputs
+
+from parity import alloc_outputs, fetch, gpu_run, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def _commit_gpu(sv, acc, out, cu, toks, lens, ragged, gamma=None, with_extras=True, stride_pad=0):
+    import torch
+    B = acc.shape[0]
+    cap = toks.shape[1]
+    buf = np.zeros((B, cap + stride_pad), dtype=np.int32)
+    buf[:, :cap] = toks
+    d_buf = _dev(buf)
+    d_toks = d_buf[:, :cap]
+    d_lens = _dev(lens.astype(np.int32))
+    app = torch.full((B,), 99, dtype=torch.int32, device="cuda:0") if with_extras else None
+    nxt = torch.full((B,), 99, dtype=torch.int32, device="cuda:0") if with_extras else None
+    kw = dict(appended=app, next_token=nxt)
+    if ragged:
+        sv.commit(_dev(acc.astype(np.int32)), _dev(out.astype(np.int32)), d_toks, d_lens,
+                  cu_draft=_dev(cu.astype(np.int32)), num_draft_rows=int(cu[-1]), **kw)
+    else:
+        sv.commit(_dev(acc.astype(np.int32)), _dev(out.astype(np.int32)), d_toks, d_lens, gamma=gamma, **kw)
+    torch.cuda.synchronize()
+    full = d_buf.cpu().numpy()
+    res = dict(tokens=full[:, :cap], pad=full[:, cap:], lens=d_lens.cpu().numpy())
+    if with_extras:
+        res["appended"] = app.cpu().numpy()
+        res["next"] = nxt.cpu().numpy()
+    return res
+
+
+def _random_case(rng, B, cap, gmax, uniform):
+    if uniform:
+        g = int(rng.integers(0, gmax + 1))
+        gam = np.full(B, g)
+    else:
+        gam = rng.integers(0, gmax + 1, size=B)
+    cu = np.concatenate([[0], np.cumsum(gam)]).astype(np.int64)
+    R_t = int(cu[-1]) + B
+    acc = np.array([rng.integers(-1, gg + 2) for gg in gam], dtype=np.int64)   # includes n > gamma
+    out = rng.integers(0, 200000, size=R_t).astype(np.int64)
+    toks = rng.integers(0, 200000, size=(B, cap)).astype(np.int32)
+    lens = rng.integers(-1, cap + 1, size=B).astype(np.int32)
+    return gam, cu, acc, out, toks, lens
+
+
+@pytest.mark.parametrize("uniform", [True, False])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_commit_matches_oracle_random(uniform, seed):
+    rng = np.random.default_rng(100 + seed + (0 if uniform else 50))
+    B, cap, gmax = 37, 24, 7
+    sv = SpecVerify(max_batch=B, max_gamma=gmax, vocab=1000, dtype="bf16")
+    gam, cu, acc, out, toks, lens = _random_case(rng, B, cap, gmax, uniform)
+    print(f"[commit] uniform={uniform} seed={seed} B={B} cap={cap}", flush=True)
+    got = _commit_gpu(sv, acc, out, cu, toks, lens, ragged=not uniform, gamma=int(gam[0]), stride_pad=5)
+    et, el, ea, en = commit_reference(acc, out, cu, toks, lens, cap)
+    assert np.array_equal(got["tokens"], et)
+    assert np.array_equal(got["lens"], el)
+    assert np.array_equal(got["appended"], ea)
+    assert np.array_equal(got["next"], en)
+    assert not got["pad"].any()   # nothing written past a row's capacity
+
+
+def test_commit_without_optional_outputs_and_empty_batch():
+    import torch
+    rng = np.random.default_rng(5)
+    sv = SpecVerify(max_batch=8, max_gamma=4, vocab=1000, dtype="bf16")
+    gam, cu, acc, out, toks, lens = _random_case(rng, 8, 16, 4, True)
+    got = _commit_gpu(sv, acc, out, cu, toks, lens, ragged=False, gamma=int(gam[0]), with_extras=False)
+    et, el, _, _ = commit_reference(acc, out, cu, toks, lens, 16)
+    assert np.array_equal(got["tokens"], et) and np.array_equal(got["lens"], el)
+    # B = 0: nothing to do, nothing touched
+    empty = torch.zeros(0, dtype=torch.int32, device="cuda:0")
+    row = torch.zeros((0, 4), dtype=torch.int32, device="cuda:0")
+    sv.commit(empty, empty, row, empty, gamma=2)
+    torch.cuda.synchronize()
+
+
+def test_commit_host_errors():
+    import torch
+    sv = SpecVerify(max_batch=4, max_gamma=2, vocab=1000, dtype="bf16")
+    z = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    t = torch.zeros((4, 8), dtype=torch.int32, device="cuda:0")
+    with pytest.raises(SpecVerifyError):
+        sv.commit(torch.zeros(5, dtype=torch.int32, device="cuda:0"), z, t, z, gamma=1)   # B > max_batch
+    with pytest.raises(SpecVerifyError):
+        sv.commit(z, z, t, z, gamma=3)                                                   # gamma > max_gamma
+
+
+@pytest.mark.parametrize("name,ragged", [("b64_g4_v128256_bf16", False), ("b512_gragged1to7_v152064_bf16", True)])
+def test_commit_after_runs_grows_sequences(name, ragged):
+    """Two verification steps in a row, each committed on device; the token
+    rows and lengths equal the oracle's commits of the run's own outputs."""
+    import torch
+    batch = 64 if not ragged else 48
+    inps = [make_inputs(name, seed=s, batch=batch) for s in (0, 1)]
+    g = int(max(int(np.max(i.gammas)) for i in inps))
+    sv = SpecVerify(max_batch=batch, max_gamma=g, vocab=inps[0].workload.vocab, dtype=inps[0].workload.dtype)
+    cap = 3 + 2 * (g + 1)
+    rng = np.random.default_rng(9)
+    toks = np.zeros((batch, cap), dtype=np.int32)
+    lens = rng.integers(1, 4, size=batch).astype(np.int32)
+    for b in range(batch):
+        toks[b, :lens[b]] = rng.integers(0, 1000, size=lens[b])
+    d_toks, d_lens = _dev(toks), _dev(lens)
+    app = torch.zeros(batch, dtype=torch.int32, device="cuda:0")
+    nxt = torch.zeros(batch, dtype=torch.int32, device="cuda:0")
+    ref_t, ref_l = toks, lens
+    for k, inp in enumerate(inps):
+        print(f"[commit] {name} step {k}", flush=True)
+        dev = to_device(inp)
+        out = alloc_outputs(inp, diagnostics=False)
+        gpu_run(sv, dev, out, inp, ragged=ragged)
+        if ragged:
+            sv.commit(out["accepted_len"], out["out_tokens"], d_toks, d_lens, cu_draft=dev["cu_draft"],
+                      num_draft_rows=int(inp.cu_draft[-1]), appended=app, next_token=nxt)
+        else:
+            sv.commit(out["accepted_len"], out["out_tokens"], d_toks, d_lens, gamma=inp.uniform_gamma,
+                      appended=app, next_token=nxt)
+        got = fetch(out)
+        ref_t, ref_l, ea, en = commit_reference(got["accepted_len"], got["out_tokens"], inp.cu_draft,
+                                                ref_t, ref_l, cap)
+        assert np.array_equal(app.cpu().numpy(), ea)
+        assert np.array_equal(nxt.cpu().numpy(), en)
+        assert (ea > 0).all()   # every sequence of these workloads is valid and fits
+    assert np.array_equal(d_toks.cpu().numpy(), ref_t)
+    assert np.array_equal(d_lens.cpu().numpy(), ref_l)
