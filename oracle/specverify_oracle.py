@@ -145,17 +145,29 @@ def _sequence_valid(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray,
     return True
 
 
-def verify_sequence(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int],
+def verify_sequence(target: np.ndarray, draft: Optional[np.ndarray], tokens: Sequence[int],
                     u: Sequence[float], T: float) -> SequenceResult:
     """Verify one sequence.
 
     target: [gamma+1, V] float64 logits; draft: [gamma, V]; tokens: [gamma]
     drafted ids; u: [gamma+1] uniforms in [0, 1); T: temperature (0 = greedy).
+
+    draft None: token-only drafts.  An n-gram or token-matching drafter gives
+    no distribution (velog "6-1편. Speculative Decoding", section 4 "그 이후
+    등장한 아이디어들: Mq 모델", N-gram; "How to Scale Your Model -- All About
+    Transformer Inference", Appendix D, the drafter options).  The draft
+    distribution is then the point mass q_i = delta_{x_i}, and every step below
+    applies unchanged: accept with probability min(1, p(x) / 1) = p(x); the
+    residual max(0, p - delta_x) is p with x removed; beta = p(x); the draft's
+    argmax (greedy) is x.
     """
     target = np.asarray(target, dtype=np.float64)
-    draft = np.asarray(draft, dtype=np.float64).reshape(-1, target.shape[1])
     tokens = np.asarray(tokens, dtype=np.int64).reshape(-1)
     u = np.asarray(u, dtype=np.float64).reshape(-1)
+    token_only = draft is None
+    if token_only:
+        draft = np.zeros((tokens.shape[0], target.shape[1]))   # only checked for validity: finite
+    draft = np.asarray(draft, dtype=np.float64).reshape(-1, target.shape[1])
     gamma, V = draft.shape[0], target.shape[1]
     assert target.shape[0] == gamma + 1 and tokens.shape[0] == gamma and u.shape[0] == gamma + 1
     nan = np.full(gamma, np.nan)
@@ -165,7 +177,7 @@ def verify_sequence(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int]
     if T == 0.0:
         # Greedy verification: the distributions are one-hot at the argmax.
         at = [argmax_first(target[i]) for i in range(gamma + 1)]
-        ad = [argmax_first(draft[i]) for i in range(gamma)]
+        ad = [int(tokens[i]) if token_only else argmax_first(draft[i]) for i in range(gamma)]
         p_x = np.array([1.0 if tokens[i] == at[i] else 0.0 for i in range(gamma)])
         q_x = np.array([1.0 if tokens[i] == ad[i] else 0.0 for i in range(gamma)])
         beta = np.array([1.0 if at[i] == ad[i] else 0.0 for i in range(gamma)])
@@ -178,7 +190,10 @@ def verify_sequence(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int]
         return SequenceResult(n, out, p_x, q_x, beta, 1.0 - beta, [], np.inf, 1.0, False, True)
 
     p = [softmax_t(target[i], T) for i in range(gamma + 1)]
-    q = [softmax_t(draft[i], T) for i in range(gamma)]
+    if token_only:
+        q = [np.eye(1, V, int(tokens[i]))[0] for i in range(gamma)]
+    else:
+        q = [softmax_t(draft[i], T) for i in range(gamma)]
     p_x = np.array([p[i][tokens[i]] for i in range(gamma)])
     q_x = np.array([q[i][tokens[i]] for i in range(gamma)])
     beta = np.array([np.sum(np.minimum(p[i], q[i])) for i in range(gamma)])
@@ -210,10 +225,11 @@ def verify_sequence(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int]
                           float(np.sum(w)), fallback, False)
 
 
-def verify_batch(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray,
+def verify_batch(target: np.ndarray, draft: Optional[np.ndarray], draft_tokens: np.ndarray,
                  uniforms: np.ndarray, temperatures: np.ndarray, cu_draft: np.ndarray,
                  dtype: str, sequences: Optional[Sequence[int]] = None):
-    """Verify a packed batch (the layout of the C ABI).
+    """Verify a packed batch (the layout of the C ABI).  ``draft`` None:
+    token-only drafts (see ``verify_sequence``).
 
     Returns (accepted_len [B], out_tokens [R_t], p_x, q_x, beta, resid
     [R_d] each, per-sequence results).  ``sequences`` restricts the work to a
@@ -232,7 +248,7 @@ def verify_batch(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray
         t0 = d0 + b
         g = d1 - d0
         res = verify_sequence(decode_logits(target[t0:t0 + g + 1], dtype),
-                              decode_logits(draft[d0:d1], dtype),
+                              None if draft is None else decode_logits(draft[d0:d1], dtype),
                               draft_tokens[d0:d1], uniforms[t0:t0 + g + 1],
                               float(temperatures[b]))
         results[b] = res

@@ -424,3 +424,107 @@ def test_partial_neginf_rows_are_valid():
     lt[:, :6] = -np.inf
     r = verify_sequence(lt, ld, [2], [0.3, 0.6], 1.0)   # p(2) = 0 -> reject
     assert r.n == 0 and r.tokens[0] >= 6 and r.p_x[0] == 0.0
+
+
+# ---------------------------------------------------------------- token-only drafts (q = delta_x)
+
+def _p(logits, T=1.0):
+    z = np.asarray(logits, dtype=np.float64) / T
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+@pytest.mark.parametrize("seed", [10, 11])
+def test_token_only_acceptance_measure_is_p_of_x(seed):
+    """With q = delta_x, min(1, p(x)/q(x)) = p(x): the accepting u_0 have measure p(x)."""
+    rng = np.random.default_rng(seed)
+    V = 6
+    lt = rng.normal(size=(2, V)) * 1.5
+    p = _p(lt[0])
+    us = _ugrid(4000)
+    for x in range(V):
+        acc = np.mean([verify_sequence(lt, None, [x], [u, 0.5], 1.0).n == 1 for u in us])
+        assert acc == pytest.approx(p[x], abs=2.5e-4)
+
+
+def test_token_only_residual_is_p_without_x():
+    """After a rejection the sample is p with x removed, renormalised: max(0, p - delta_x)."""
+    rng = np.random.default_rng(12)
+    V = 5
+    lt = rng.normal(size=(2, V)) * 1.5
+    p = _p(lt[0])
+    x = int(np.argmax(p))
+    want = p.copy()
+    want[x] = 0.0
+    want /= want.sum()
+    counts = np.zeros(V)
+    for u in _ugrid(10000):
+        r = verify_sequence(lt, None, [x], [0.999999, u], 1.0)
+        if r.n == 0:
+            counts[r.tokens[0]] += 1
+    assert counts.sum() == 10000            # u_0 = 0.999999 >= p(x): always rejected
+    np.testing.assert_allclose(counts / counts.sum(), want, atol=1e-4)
+
+
+def test_token_only_diagnostics_closed_form():
+    """q(x) = 1, beta = sum min(p, delta_x) = p(x), Z = sum max(0, p - delta_x) = 1 - p(x)."""
+    rng = np.random.default_rng(13)
+    lt = rng.normal(size=(4, 40)) * 2.0
+    toks = [3, 17, 39]
+    r = verify_sequence(lt, None, toks, [0.3, 0.2, 0.9, 0.5], 0.8)
+    p = [_p(lt[i], 0.8) for i in range(3)]
+    for i, x in enumerate(toks):
+        assert r.q_x[i] == 1.0
+        assert r.p_x[i] == pytest.approx(p[i][x], rel=1e-12)
+        assert r.beta[i] == pytest.approx(p[i][x], rel=1e-12)
+        assert r.resid[i] == pytest.approx(1.0 - p[i][x], rel=1e-12)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_token_only_equals_point_mass_draft_logits(T):
+    """A token-only draft is the draft whose logits are 0 at x and -inf elsewhere
+    (its softmax is exactly delta_x): the two give identical results."""
+    rng = np.random.default_rng(14)
+    V, g = 30, 4
+    for _ in range(40):
+        lt = rng.normal(size=(g + 1, V)) * 2.0
+        toks = rng.integers(0, V, size=g)
+        ld = np.full((g, V), -np.inf)
+        ld[np.arange(g), toks] = 0.0
+        u = rng.random(g + 1)
+        a = verify_sequence(lt, None, toks, u, T)
+        b = verify_sequence(lt, ld, toks, u, T)
+        assert (a.n, a.tokens) == (b.n, b.tokens)
+        for k in ("p_x", "q_x", "beta", "resid"):
+            np.testing.assert_allclose(getattr(a, k), getattr(b, k), rtol=1e-12, atol=1e-15)
+
+
+def test_token_only_output_law_is_p():
+    """Whatever token-only drafter proposes x_0 (law r), the first emitted token
+    has law p_0: enumeration of x_0, with the acceptance measured on a u_0 grid
+    and the residual law on a u_1 grid (velog 2-3, item 3: P(x = x') = p(x'))."""
+    rng = np.random.default_rng(15)
+    V = 4
+    lt = rng.normal(size=(2, V))
+    P0 = _p(lt[0])
+    r = np.array([0.5, 0.1, 0.3, 0.1])     # any drafter's law over x_0
+    us = _ugrid(4000)
+    first = np.zeros(V)
+    for x0 in range(V):
+        acc = np.mean([verify_sequence(lt, None, [x0], [u, 0.5], 1.0).n == 1 for u in us])
+        law = np.zeros(V)
+        for u in us:
+            res = verify_sequence(lt, None, [x0], [0.999999, u], 1.0)
+            assert res.n == 0
+            law[res.tokens[0]] += 1.0 / len(us)
+        first[x0] += r[x0] * acc
+        first += r[x0] * (1.0 - acc) * law
+    np.testing.assert_allclose(first, P0, atol=1e-3)
+
+
+def test_token_only_greedy_is_argmax_comparison():
+    lt = np.array([[0.0, 3.0, 1.0], [2.0, 0.0, 0.0], [0.0, 0.0, 5.0]])
+    r = verify_sequence(lt, None, [1, 2], [0.5, 0.5, 0.5], 0.0)
+    assert r.n == 1 and r.tokens == [1, 0]                 # argmax of row 1 is 0, not 2
+    assert r.q_x.tolist() == [1.0, 1.0]
+    assert r.beta.tolist() == [1.0, 0.0] and r.resid.tolist() == [0.0, 1.0]
