@@ -273,6 +273,29 @@ def main():
     stream_ms = ks / nrec
     finish_ms = kf / nrec
 
+    # Token-only drafts (draft logits NULL, q_i = delta_{x_i}) on the same batch:
+    # only the target rows are read.
+    def step_tok(k):
+        t, _ = copies[k % ncopy]
+        sv.run(t, None, tokens, uniforms, temps, **out, **gamma_kw)
+
+    for k in range(args.warmup):
+        step_tok(k)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for k in range(args.steps):
+        step_tok(k)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    tok_ms = ev0.elapsed_time(ev1) / args.steps
+    sv.set_timing(True)
+    for k in range(args.steps):
+        step_tok(k)
+    tn, tks, tkf = sv.timing_totals()
+    sv.set_timing(False)
+    tok_bytes = int(inp.target.nbytes)
+    tok_stream_ms = tks / tn
+
     # The on-device commit of a step (specverify_commit): K commits of the last
     # step's outputs into token rows with room for all of them, between two
     # events on the launch stream.
@@ -334,6 +357,13 @@ def main():
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic, "kernel": "stream_kernel",
                      "alg_bytes_per_launch": logit_bytes, "kernel_launches_timed": nrec},
         "step_GBps": alg_bytes / (ms * 1e-3) / 1e9,
+        "token_only": {"ms_per_step": tok_ms, "value": R_t / (tok_ms * 1e-3), "unit": "rows/s",
+                       "logits_GBps": tok_bytes / (tok_ms * 1e-3) / 1e9,
+                       "kernel_ms": {"stream": tok_stream_ms, "finish": tkf / tn},
+                       "roofline": {"bound": "hbm", "achieved": tok_bytes / (tok_stream_ms * 1e-3) / 1e9,
+                                    "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                    "frac": tok_bytes / (tok_stream_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                    "alg_bytes_per_launch": tok_bytes}},
         "commit": {"kernel": "commit_kernel", "us_per_call": commit_us, "sequences": B,
                    # reads accepted_len, out_tokens, seq_lens; writes at most R_t tokens
                    # and seq_lens, appended, next_token
@@ -343,6 +373,8 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
         res["commit"]["cpu_oracle_us_per_call"] = cpu_commit_baseline(inp, out, cap)
+        from rejection_sampling_verifier_specverify_amd.workloads import token_only
+        res["token_only"]["cpu_baseline"] = cpu_baseline(token_only(inp), min(args.cpu_seconds, 5.0))
     sv.close()
     print(json.dumps(res), flush=True)
 

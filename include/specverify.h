@@ -20,6 +20,15 @@
  * Sonar through speculation", section "단일 토큰에 대한 MTP 스케줄링": the
  * sync on the accepted length is what extra GPU work avoids).
  *
+ * Token-only drafts.  A drafter that proposes tokens without a distribution
+ * (an n-gram or token-matching drafter: velog "6-1편. Speculative Decoding",
+ * section 4, N-gram; "How to Scale Your Model", Appendix D) passes
+ * draft_logits = NULL with its tokens.  Its distribution is then the point
+ * mass q_i = delta_{x_i}, and the same rule gives: accept while u_i < p_i(x_i);
+ * the residual is p_n without x_n, renormalised; q(x) = 1, beta = p(x),
+ * Z = 1 - p(x); greedy (T = 0) accepts while x_i is the target argmax.  Only
+ * the target logits are read.
+ *
  * Packed ragged layout.  Sequence b owns draft rows cu_draft[b] ..
  * cu_draft[b+1] - 1 and target rows cu_t[b] .. cu_t[b] + gamma_b with
  * cu_t[b] = cu_draft[b] + b (so R_t = R_d + B target rows in total).
@@ -98,7 +107,7 @@ typedef struct {
                                  multiple of 16 the kernels use 16-byte loads, else
                                  element loads                                      */
   int64_t target_stride;      /* elements between rows, >= V                       */
-  const void* draft_logits;   /* [R_d, draft_stride]; may be NULL iff R_d == 0     */
+  const void* draft_logits;   /* [R_d, draft_stride]; NULL = token-only drafts      */
   int64_t draft_stride;
   const int32_t* draft_tokens;/* [R_d] drafted ids x_i; may be NULL iff R_d == 0   */
   const float* uniforms;      /* [R_t] u in [0,1): uniforms[cu_t[b]+i], i < gamma_b,

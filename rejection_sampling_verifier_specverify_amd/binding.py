@@ -205,13 +205,15 @@ class SpecVerify:
             inp.gamma = 0
             inp.cu_draft = _ptr(cu_draft)
             inp.num_draft_rows = int(num_draft_rows if num_draft_rows is not None
-                                     else (draft.shape[0] if draft is not None else 0))
+                                     else (draft_tokens.shape[0] if draft_tokens is not None else 0))
         inp.target_logits = _ptr(target)
         inp.target_stride = int(target.stride(0))
+        # draft None with drafted tokens: token-only drafts (q_i = delta_{x_i})
         has_draft = draft is not None and draft.numel() > 0
         inp.draft_logits = _ptr(draft) if has_draft else None
         inp.draft_stride = int(draft.stride(0)) if has_draft else int(self.vocab)
-        inp.draft_tokens = _ptr(draft_tokens) if has_draft else None
+        has_tokens = draft_tokens is not None and draft_tokens.numel() > 0
+        inp.draft_tokens = _ptr(draft_tokens) if has_tokens else None
         inp.uniforms = _ptr(uniforms)
         inp.temperatures = _ptr(temperatures)
         out = Outputs(_ptr(accepted_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),

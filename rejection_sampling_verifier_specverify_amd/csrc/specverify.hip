@@ -131,6 +131,7 @@ struct Params {
   int32_t max_gamma;
   uint32_t epoch;
   int32_t spin_limit;
+  int32_t token_only;        // drafts come without logits: q_i = delta_{x_i}
   uint32_t div_c[3];         // unsigned division by C: multiplier and two shifts
   uint32_t div_g[3];         // unsigned division by gamma + 1 (uniform gamma)
   uint64_t* xch1;            // [rows][C][kX1] tagged slots
@@ -560,7 +561,8 @@ __device__ __forceinline__ Item make_item(const Params& P, int grp, int idx, int
   } else if (m.T == 0.0f) {
     mode = 2;
   }   // any other temperature is invalid data: nothing is read
-  it.rdf = (uint32_t)m.rd | (mode << 24) | ((uint32_t)(m.pair != 0) << 26);
+  // a token-only draft has no logits: its position streams like one without a draft
+  it.rdf = (uint32_t)m.rd | (mode << 24) | ((uint32_t)(m.pair != 0 && !P.token_only) << 26);
   return it;
 }
 
@@ -883,6 +885,8 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
   const uint32_t tag = P.epoch;
   const float s = kLog2e / T;
   const float ninf = -__builtin_huge_valf();
+  // dp: the draft's logits are there; tk: a token-only draft, q = delta_x
+  const bool dp = pair && !P.token_only, tk = pair && P.token_only;
   const int x = pair ? ld_const(P.tokens, rd) : 0;
   const bool x_ok = x >= 0 && x < P.V;
   RowSlots<NPER> q;
@@ -896,7 +900,7 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
     W[j] = 0.0f;
     Bp[j] = 0.0f;
     const int c = lane + 64 * j;
-    if (pair && c < C) {
+    if (dp && c < C) {
       const float4 pt = *(const float4*)(P.part + ((int64_t)r * C + c) * kPart);
       done &= __float_as_uint(pt.x) == tag;
       W[j] = pt.y;
@@ -906,23 +910,42 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
   float lx = 0.0f, dx = 0.0f;
   if (pair && x_ok) {
     lx = load_logit<DT>(P.target, r, P.tstride_b, x);
-    dx = load_logit<DT>(P.draft, rd, P.dstride_b, x);
+    if (dp) dx = load_logit<DT>(P.draft, rd, P.dstride_b, x);
   }
-  if (!slots_ready(q, C, tag, pair ? 4 : 2, lane) || !__all(done)) return row_payload(2, false, 0);
+  if (!slots_ready(q, C, tag, dp ? 4 : 2, lane) || !__all(done)) return row_payload(2, false, 0);
   float Mt, St, Md = ninf, Sd = 0.0f;
   merge_row(q, C, 0, s, lane, Mt, St);
-  if (pair) merge_row(q, C, 2, s, lane, Md, Sd);
-  if (!norm_ok(Mt, St) || (pair && (!norm_ok(Md, Sd) || !x_ok))) return row_payload(1, false, 0);
+  if (dp) merge_row(q, C, 2, s, lane, Md, Sd);
+  if (!norm_ok(Mt, St) || (dp && !norm_ok(Md, Sd)) || (pair && !x_ok)) return row_payload(1, false, 0);
+  const int cx = x / F::CH;              // the chunk that holds x
+  const int lxl = cx & 63, jx = cx >> 6;
   // per-chunk scales, residual mass, beta, and the masses the final sample reads
   float at[NPER], tot[NPER], mt[NPER], md[NPER], rho[NPER];
-  float zl = 0.0f, bl = 0.0f;
 #pragma unroll
   for (int j = 0; j < NPER; ++j) {
     const bool in = lane + 64 * j < C;
     mt[j] = in ? slot_f(q.w[j][0]) : ninf;
-    md[j] = (in && pair) ? slot_f(q.w[j][2]) : ninf;
+    md[j] = (in && dp) ? slot_f(q.w[j][2]) : ninf;
     at[j] = in ? chunk_scale(mt[j], Mt, St, s) : 0.0f;
-    rho[j] = (in && pair) ? chunk_rho(mt[j], Mt, St, md[j], Md, Sd, s) : 0.0f;
+    rho[j] = (in && dp) ? chunk_rho(mt[j], Mt, St, md[j], Md, Sd, s) : 0.0f;
+  }
+  const float mtx = lane_f(pick(mt, jx), lxl);
+  // e at x as phase 1 computed it (the same operations on the same values)
+  const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(lx, s, chunk_offset(mtx, s)));
+  if (tk) {
+    // the residual p - delta_x is p without x: the chunk sums of e_t, less
+    // x's own e in its chunk
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      const bool in = lane + 64 * j < C;
+      W[j] = in ? slot_f(q.w[j][1]) : 0.0f;
+      if (lane + 64 * j == cx) W[j] = fmaxf(W[j] - ex, 0.0f);
+    }
+  }
+  float zl = 0.0f, bl = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const bool in = lane + 64 * j < C;
     zl += in ? at[j] * W[j] : 0.0f;
     bl += in ? at[j] * Bp[j] : 0.0f;
   }
@@ -934,11 +957,10 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
   // p(x), q(x): the logits at x with their chunk's offset and scale; the
   // acceptance test u q(x) < p(x)
   if (pair) {
-    const int cx = x / F::CH;
-    const int lxl = cx & 63, jx = cx >> 6;
-    const float mtx = lane_f(pick(mt, jx), lxl), mdx = lane_f(pick(md, jx), lxl);
-    const float px = chunk_scale(mtx, Mt, St, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(lx, s, chunk_offset(mtx, s)));
-    const float qx = chunk_scale(mdx, Md, Sd, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(dx, s, chunk_offset(mdx, s)));
+    const float mdx = lane_f(pick(md, jx), lxl);
+    const float px = chunk_scale(mtx, Mt, St, s) * ex;
+    const float qx = tk ? 1.0f : chunk_scale(mdx, Md, Sd, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(dx, s, chunk_offset(mdx, s)));
+    if (tk) beta = px;   // sum min(p, delta_x) = p(x)
     if (lane == 0) {
       if (P.p_draft) P.p_draft[rd] = px;
       if (P.q_draft) P.q_draft[rd] = qx;
@@ -996,7 +1018,8 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
   const int nb = P.V * F::ESIZE;
   u32x4 R[2][kU];
   issue_row<DT, VEC>(row_rsrc(P.target, r, P.tstride_b, nb), cs, lane, R[0]);
-  issue_row<DT, VEC>(row_rsrc(P.draft, resid ? rd : 0, P.dstride_b, resid ? nb : 0), cs, lane, R[1]);
+  const bool rd_read = resid && dp;
+  issue_row<DT, VEC>(row_rsrc(P.draft, rd_read ? rd : 0, P.dstride_b, rd_read ? nb : 0), cs, lane, R[1]);
   float w[F::L], ld[F::L];
   unpack<DT>(R[0], w);
   unpack<DT>(R[1], ld);
@@ -1004,7 +1027,10 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
 #pragma unroll
   for (int k = 0; k < F::L; ++k) {
     const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(w[k], s, ct));
-    w[k] = resid ? resid_w(et, __builtin_amdgcn_exp2f(__builtin_fmaf(ld[k], s, cd)), rho_s) : et;
+    if (tk && resid)
+      w[k] = token_of<DT>(cs, k, lane) == x ? 0.0f : et;   // p without x
+    else
+      w[k] = resid ? resid_w(et, __builtin_amdgcn_exp2f(__builtin_fmaf(ld[k], s, cd)), rho_s) : et;
   }
   // Running sums in the chunk's units against tau = (thr - before) / a_s.
   // Token order inside the chunk is round u, then lane, then element: a
@@ -1049,11 +1075,13 @@ template <int NPER>
 __device__ __forceinline__ uint32_t finish_greedy(const Params& P, int r, int rd, bool pair, int lane) {
   const int C = P.C;
   const uint32_t tag = P.epoch;
+  // dp: the draft's logits are there; a token-only draft's argmax is x itself
+  const bool dp = pair && !P.token_only;
   RowSlots<NPER> q;
   uint32_t soff[NPER];
   slot_offsets(C, lane, soff);
   slots_issue(P, r, true, soff, q);
-  if (!slots_ready(q, C, tag, pair ? 4 : 2, lane)) return row_payload(2, false, 0);
+  if (!slots_ready(q, C, tag, dp ? 4 : 2, lane)) return row_payload(2, false, 0);
   float av = -__builtin_huge_valf(), dv = -__builtin_huge_valf();
   int ak = 0x7FFFFFFF, dk = 0x7FFFFFFF, bad = 0;
 #pragma unroll
@@ -1061,7 +1089,7 @@ __device__ __forceinline__ uint32_t finish_greedy(const Params& P, int r, int rd
     if (lane + 64 * j < C) {
       argmax_merge(av, ak, slot_f(q.w[j][0]), (int)(uint32_t)q.w[j][1]);
       bad |= (uint32_t)q.w[j][1] == 0xFFFFFFFFu;
-      if (pair) {
+      if (dp) {
         argmax_merge(dv, dk, slot_f(q.w[j][2]), (int)(uint32_t)q.w[j][3]);
         bad |= (uint32_t)q.w[j][3] == 0xFFFFFFFFu;
       }
@@ -1070,12 +1098,13 @@ __device__ __forceinline__ uint32_t finish_greedy(const Params& P, int r, int rd
   bad = __any(bad);
   wave_argmax(av, ak);
   wave_argmax(dv, dk);
-  if (bad || av == -__builtin_huge_valf() || (pair && dv == -__builtin_huge_valf()))
+  if (bad || av == -__builtin_huge_valf() || (dp && dv == -__builtin_huge_valf()))
     return row_payload(1, false, 0);
   bool acc = false;
   if (pair) {
     const int x = ld_const(P.tokens, rd);
     if (x < 0 || x >= P.V) return row_payload(1, false, 0);
+    if (!dp) dk = x;
     acc = (x == ak);
     if (lane == 0) {
       if (P.p_draft) P.p_draft[rd] = (x == ak) ? 1.0f : 0.0f;
@@ -1346,16 +1375,18 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   if (!in->target_logits || !in->uniforms || !in->temperatures || !out->accepted_len ||
       !out->out_tokens)
     return SPECVERIFY_ERR_INVALID_ARGUMENT;
-  if (R_d > 0 && (!in->draft_logits || !in->draft_tokens)) return SPECVERIFY_ERR_INVALID_ARGUMENT;
-  if (in->target_stride < V || (R_d > 0 && in->draft_stride < V)) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  if (R_d > 0 && !in->draft_tokens) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  // drafts without logits are token-only drafts: q_i = delta_{x_i}
+  const bool has_dl = R_d > 0 && in->draft_logits != nullptr;
+  if (in->target_stride < V || (has_dl && in->draft_stride < V)) return SPECVERIFY_ERR_INVALID_ARGUMENT;
   const int esize = h->cfg.dtype == SPECVERIFY_F32 ? 4 : 2;
-  if (((uintptr_t)in->target_logits % esize) || (R_d > 0 && ((uintptr_t)in->draft_logits % esize)))
+  if (((uintptr_t)in->target_logits % esize) || (has_dl && ((uintptr_t)in->draft_logits % esize)))
     return SPECVERIFY_ERR_UNSUPPORTED;   // logits must be element aligned
   // 16-byte loads need rows and the row length on 16-byte boundaries;
   // otherwise the kernels read element by element.
   const bool vec = !((uintptr_t)in->target_logits & 15) && !((in->target_stride * esize) & 15) &&
                    !(((int64_t)V * esize) & 15) &&
-                   (R_d == 0 || (!((uintptr_t)in->draft_logits & 15) && !((in->draft_stride * esize) & 15)));
+                   (!has_dl || (!((uintptr_t)in->draft_logits & 15) && !((in->draft_stride * esize) & 15)));
 
   // Persistent grid: per row group, as many waves as the device holds, never
   // more than the busiest group has items.
@@ -1391,6 +1422,7 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   P.max_gamma = h->cfg.max_gamma;
   P.epoch = h->epoch;
   P.spin_limit = h->cfg.spin_limit;
+  P.token_only = R_d > 0 && !has_dl;
   udiv_consts((uint32_t)C, P.div_c);
   udiv_consts((uint32_t)(in->cu_draft ? 1 : in->gamma + 1), P.div_g);
   P.xch1 = h->xch1;

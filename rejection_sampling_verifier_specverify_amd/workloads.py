@@ -39,7 +39,7 @@ from typing import Optional, Sequence, Tuple, Union
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "HEADLINE", "Inputs", "make_inputs",
+    "Workload", "WORKLOADS", "HEADLINE", "Inputs", "make_inputs", "token_only",
     "f32_to_bf16_bits", "bf16_bits_to_f32",
 ]
 
@@ -90,7 +90,7 @@ class Inputs:
     workload: Workload
     seed: int
     target: np.ndarray        # [R_t, V]
-    draft: np.ndarray         # [R_d, V]
+    draft: Optional[np.ndarray]   # [R_d, V]; None: token-only drafts
     draft_tokens: np.ndarray  # [R_d] int32
     uniforms: np.ndarray      # [R_t] float32
     temperatures: np.ndarray  # [B] float32
@@ -117,7 +117,7 @@ class Inputs:
 
     @property
     def logit_bytes(self) -> int:
-        return int(self.target.nbytes + self.draft.nbytes)
+        return int(self.target.nbytes + (self.draft.nbytes if self.draft is not None else 0))
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -236,3 +236,10 @@ def make_custom(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int],
                   np.asarray(tokens, dtype=np.int32).reshape(-1),
                   np.asarray(uniforms, dtype=np.float32).reshape(-1),
                   np.asarray(temperatures, dtype=np.float32).reshape(-1), cu)
+
+
+def token_only(inp: Inputs) -> Inputs:
+    """The same batch with token-only drafts: the drafted tokens stay (they
+    were drawn from the draft distribution, one possible drafter's law) and
+    the draft logits are dropped, so q_i = delta_{x_i}."""
+    return dataclasses.replace(inp, draft=None)

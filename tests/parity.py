@@ -40,7 +40,7 @@ def to_device(inp, device="cuda:0"):
         return torch.from_numpy(a).to(device)
     return dict(
         target=logits(inp.target),
-        draft=logits(inp.draft),
+        draft=logits(inp.draft) if inp.draft is not None else None,
         draft_tokens=torch.from_numpy(inp.draft_tokens).to(device),
         uniforms=torch.from_numpy(inp.uniforms).to(device),
         temperatures=torch.from_numpy(inp.temperatures).to(device),

@@ -24,7 +24,7 @@ def _handle(inp, **kw):
 
 def _check(inp, sequences=None, ragged=None, label=""):
     print(f"[parity] {label} B={inp.batch} V={inp.workload.vocab} dtype={inp.workload.dtype} "
-          f"rows={inp.target.shape[0]}+{inp.draft.shape[0]}", flush=True)
+          f"rows={inp.target.shape[0]}+{inp.draft.shape[0] if inp.draft is not None else 'tokens'}", flush=True)
     sv = _handle(inp)
     dev = to_device(inp)
     out = alloc_outputs(inp)
@@ -344,3 +344,55 @@ def test_host_validation_errors():
     with pytest.raises(SpecVerifyError) as e:
         SpecVerify(max_batch=1, max_gamma=1, vocab=524289, dtype="f32")
     assert e.value.status == ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- token-only drafts (q = delta_x)
+
+from rejection_sampling_verifier_specverify_amd.workloads import token_only  # noqa: E402
+
+
+@pytest.mark.parametrize("name,batch", [("b64_g4_v128256_bf16", 16), ("b256_g8_v128256_bf16_mixedT", 24),
+                                        ("b32_g1_v129280_bf16_mtp", 32), ("b1_g4_v32000_f32", None),
+                                        ("b512_gragged1to7_v152064_bf16", 40)])
+def test_token_only_workloads(name, batch):
+    inp = token_only(make_inputs(name, seed=3, batch=batch))
+    _check(inp, label=f"token-only {name}")
+
+
+@pytest.mark.parametrize("V,dtype", [(1, "bf16"), (63, "bf16"), (2049, "bf16"), (20007, "bf16"),
+                                     (131080, "f32"), (262144, "bf16")])
+def test_token_only_vocab_shapes(V, dtype):
+    inp = token_only(_rand_custom(V, [3, 0, 2, 4], [0.9, 1.0, 0.0, 0.7], seed=V + 1, dtype=dtype))
+    _check(inp, label=f"token-only V={V} {dtype}")
+
+
+def test_token_only_point_mass_edges():
+    """x the only finite logit of its chunk (its chunk's residual is empty), and
+    p(x) ~ 1 (Z ~ 0)."""
+    V = 6000                              # fp32: chunks of 1024 logits
+    rng = np.random.default_rng(21)
+    tgt = rng.normal(size=(5, V)) * 2.0
+    tgt[0, 2048:4096] = -np.inf           # chunks 2 and 3 of row 0: only x = 3000 is finite
+    tgt[0, 3000] = 1.0
+    tgt[1, :] = -30.0                     # row 1: x = 5999 carries almost all of p
+    tgt[1, 5999] = 30.0
+    drf = tgt[[0, 1, 3]] + rng.normal(size=(3, V))
+    toks = np.array([3000, 5999, 17], dtype=np.int32)
+    u = np.array([0.99, 0.5, 0.3, 0.999, 0.4], dtype=np.float32)
+    base = make_custom(tgt, drf, toks, u, [1.0, 1.0], [2, 1])
+    _check(token_only(base), label="token-only edges")
+
+
+def test_token_only_one_poll_budget_bit_exact():
+    inp = token_only(_rand_custom(128256, [4] * 12, [0.9] * 12, seed=77))
+    dev = to_device(inp)
+    a = _handle(inp, spin_limit=1)
+    b = _handle(inp)
+    oa, ob = alloc_outputs(inp), alloc_outputs(inp)
+    gpu_run(a, dev, oa, inp)
+    gpu_run(b, dev, ob, inp)
+    ga, gb = fetch(oa), fetch(ob)
+    for k in ga:
+        assert np.array_equal(ga[k], gb[k], equal_nan=True), k
+    rep = compare(inp, ga)
+    assert rep.ok(), rep.summary()
