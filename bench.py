@@ -89,6 +89,9 @@ def _pmc_rows(folder: str, counter: str):
     return sorted(out)
 
 
+PROBE_COPIES = 5   # plain copies of the logits' size that --copy-probe dispatches last
+
+
 def summarize_pmc(args):
     """HBM traffic per launch of stream_kernel: FETCH_SIZE and WRITE_SIZE (KiB
     per dispatch) averaged over its dispatches, each scaled by bytes / counter
@@ -104,7 +107,9 @@ def summarize_pmc(args):
         if not ker:
             raise SystemExit(f"{name}: no stream_kernel dispatch in {folder}")
         last = max(d for d, _ in ker)
-        cp = [v for d, k, v in rows if d > last and "copy" in k.lower()]
+        # the probe's copies are the run's last ones (a small copy, such as a
+        # device-to-host read, may come between the kernel and the probe)
+        cp = [v for d, k, v in rows if d > last and "copy" in k.lower()][-PROBE_COPIES:]
         if not cp:
             raise SystemExit(f"{name}: no copy-probe dispatch after the last stream_kernel in {folder}")
         kv = float(np.mean([v for _, v in ker]))
@@ -324,7 +329,7 @@ def main():
     if args.copy_probe:   # plain copy of the logits' size, for FETCH/WRITE_SIZE calibration
         src = torch.empty(logit_bytes // 2, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(5):
+        for _ in range(PROBE_COPIES):
             dst.copy_(src)
         torch.cuda.synchronize()
 

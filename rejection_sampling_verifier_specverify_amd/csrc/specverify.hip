@@ -418,7 +418,8 @@ __device__ __forceinline__ void unpack(const u32x4 (&raw)[kU], float (&x)[Fmt<DT
 // at once: one comparison per token, and one at a time (each comparison's
 // lane mask is used at once), which keeps the scalar registers of this rare
 // path from crowding the common one.
-template <int DT>
+// TWO false: only x is masked (y may alias it).
+template <int DT, bool TWO = true>
 __device__ __forceinline__ void mask_tail2(float (&x)[Fmt<DT>::L], float (&y)[Fmt<DT>::L], int c, int V, int lane) {
   using F = Fmt<DT>;
   const int lim = V - (c * F::CH + lane * F::EPV);
@@ -428,7 +429,7 @@ __device__ __forceinline__ void mask_tail2(float (&x)[Fmt<DT>::L], float (&y)[Fm
     for (int e = 0; e < F::EPV; ++e) {
       const bool out = u * 64 * F::EPV + e >= lim;
       x[u * F::EPV + e] = out ? -__builtin_huge_valf() : x[u * F::EPV + e];
-      y[u * F::EPV + e] = out ? -__builtin_huge_valf() : y[u * F::EPV + e];
+      if (TWO) y[u * F::EPV + e] = out ? -__builtin_huge_valf() : y[u * F::EPV + e];
       __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -567,7 +568,8 @@ __device__ __forceinline__ Item make_item(const Params& P, int grp, int idx, int
 }
 
 // The item's loads: always the same 2 kU (VEC) instructions; absent rows
-// read through zero-sized buffers.
+// read through zero-sized buffers.  issue_target: the target row alone, for
+// launches without draft logits.
 template <int DT, bool VEC>
 __device__ __forceinline__ void issue_item(const Params& P, const Item& it, int lane, u32x4 (&R)[2][kU]) {
   const int nb = P.V * Fmt<DT>::ESIZE;
@@ -576,6 +578,12 @@ __device__ __forceinline__ void issue_item(const Params& P, const Item& it, int 
   const Rsrc rd = row_rsrc(P.draft, (live && it.pair()) ? it.rd() : 0, P.dstride_b, (live && it.pair()) ? nb : 0);
   issue_row<DT, VEC>(rt, it.c(), lane, R[0]);
   issue_row<DT, VEC>(rd, it.c(), lane, R[1]);
+}
+template <int DT, bool VEC>
+__device__ __forceinline__ void issue_target(const Params& P, const Item& it, int lane, u32x4 (&R)[kU]) {
+  const bool live = it.mode() != 0;
+  const Rsrc rt = row_rsrc(P.target, live ? it.r() : 0, P.tstride_b, live ? P.V * Fmt<DT>::ESIZE : 0);
+  issue_row<DT, VEC>(rt, it.c(), lane, R);
 }
 
 // Phase 1 of a sampled row: chunk max, exponentials in place, chunk sum.
@@ -653,22 +661,23 @@ __device__ __forceinline__ void greedy_row(const float (&x)[Fmt<DT>::L], int c, 
 // later (rows that were not read hold zeros).  Likewise every path ends in
 // the same one store (items with nothing to publish write the dummy slots),
 // so the count of memory operations in flight is the same on all paths.
-template <int DT>
+// D false: the launch has no draft logits; only row 0 exists.
+template <int DT, bool D = true>
 __device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lane, uint64_t* wdummy,
                                         const u32x4 (&R)[2][kU], float (&E)[2][Fmt<DT>::L], float& mt,
                                         float& md, float& st) {
   unpack<DT>(R[0], E[0]);
-  unpack<DT>(R[1], E[1]);
+  if (D) unpack<DT>(R[1], E[1]);
   uint32_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
   uint64_t* dst = wdummy;
   if (it.mode() != 0) {
     dst = P.xch1 + ((int64_t)it.r() * P.C + it.c()) * kX1;
-    if ((it.c() + 1) * Fmt<DT>::CH > P.V) mask_tail2<DT>(E[0], E[1], it.c(), P.V, lane);
+    if ((it.c() + 1) * Fmt<DT>::CH > P.V) mask_tail2<DT, D>(E[0], E[1], it.c(), P.V, lane);
     if (it.mode() == 1) {
       float sd = 0.0f;
       md = -__builtin_huge_valf();
       p1_row<DT>(E[0], it.s, mt, st);
-      if (it.pair()) p1_row<DT>(E[1], it.s, md, sd);
+      if (D && it.pair()) p1_row<DT>(E[1], it.s, md, sd);
       v0 = __float_as_uint(mt);
       v1 = __float_as_uint(st);
       v2 = __float_as_uint(md);
@@ -677,7 +686,7 @@ __device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lan
       float vt, vd = -__builtin_huge_valf();
       int kt, kd = 0x7FFFFFFF, bt, bd = 0;
       greedy_row<DT>(E[0], it.c(), lane, vt, kt, bt);
-      if (it.pair()) greedy_row<DT>(E[1], it.c(), lane, vd, kd, bd);
+      if (D && it.pair()) greedy_row<DT>(E[1], it.c(), lane, vd, kd, bd);
       v0 = __float_as_uint(vt);
       v1 = bt ? 0xFFFFFFFFu : (uint32_t)kt;
       v2 = __float_as_uint(vd);
@@ -846,6 +855,30 @@ __global__ __launch_bounds__(kStreamThreads, 2) void stream_kernel(Params P) {
   }
   // loads of items past the end read zero-sized buffers; let them land
   __builtin_amdgcn_s_waitcnt(0);
+}
+
+// The streaming pass of a launch without draft logits (token-only drafts,
+// or gamma = 0 everywhere): phase 1 alone, one item per wave.  No item reads
+// another's statistics, so nothing waits on other waves and the grid need
+// not be resident at once: it covers every item, and the dispatcher starts
+// new waves as others end (measured faster than persistent waves with one to
+// four items in flight each).
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kStreamThreads) void stream_t_kernel(Params P) {
+  using F = Fmt<DT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = (int)(blockIdx.x % kGroups);
+  const int j = (int)(blockIdx.x / kGroups) * kStreamWaves + wave;
+  const int n_items = ((P.R_t - grp + kGroups - 1) / kGroups) * P.C;
+  if (j >= n_items) return;
+  const Item it = make_item(P, grp, j, n_items);
+  if (it.mode() == 0) return;   // nothing to read or publish
+  u32x4 R[2][kU];               // row 1 is never loaded or read
+  float E[2][F::L];
+  issue_target<DT, VEC>(P, it, lane, R[0]);
+  float mt, md, st;
+  p1_item<DT, false>(P, it, lane, P.dummy, R, E, mt, md, st);
 }
 
 // ================================================================== finish kernel
@@ -1224,16 +1257,17 @@ __global__ __launch_bounds__(64 * kCommitWaves) void commit_kernel(CommitParams 
 
 typedef void (*KernelFn)(Params);
 struct Kernels {
-  KernelFn stream, finish;
+  KernelFn stream, stream_t, finish;   // stream_t: launches without draft logits
 };
 template <int DT, bool VEC>
 Kernels kernels_for(int nper) {
-  if (nper == 1) return {stream_kernel<DT, VEC, 1>, finish_kernel<DT, VEC, 1>};
-  if (nper == 2) return {stream_kernel<DT, VEC, 2>, finish_kernel<DT, VEC, 2>};
+  if (nper == 1) return {stream_kernel<DT, VEC, 1>, stream_t_kernel<DT, VEC>, finish_kernel<DT, VEC, 1>};
+  if (nper == 2) return {stream_kernel<DT, VEC, 2>, stream_t_kernel<DT, VEC>, finish_kernel<DT, VEC, 2>};
   // more than 128 chunks per row: fp32 only (the bf16 build would not fit
   // its registers)
-  if constexpr (DT == SPECVERIFY_F32) return {stream_kernel<DT, VEC, 4>, finish_kernel<DT, VEC, 4>};
-  return {nullptr, nullptr};
+  if constexpr (DT == SPECVERIFY_F32)
+    return {stream_kernel<DT, VEC, 4>, stream_t_kernel<DT, VEC>, finish_kernel<DT, VEC, 4>};
+  return {nullptr, nullptr, nullptr};
 }
 Kernels kernels_for(int dtype, bool vec, int nper) {
   if (dtype == SPECVERIFY_F32) return vec ? kernels_for<SPECVERIFY_F32, true>(nper) : kernels_for<SPECVERIFY_F32, false>(nper);
@@ -1310,19 +1344,23 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cfg->device);
   // A stream kernel that spilled to scratch would make the runtime allocate
   // scratch at its first launch and spill in its inner loop: such a build is
-  // refused rather than run.
-  for (int v = 0; v < 2 && e == hipSuccess; ++v) {
-    const void* fn = (const void*)kernels_for(cfg->dtype, v == 1, h->nper).stream;
-    int per_cu = 0;
+  // refused rather than run.  (The kernel without draft logits never waits
+  // on other waves: its grid is not persistent and needs no residency.)
+  int capmax = 0;
+  for (int v = 0; v < 4 && e == hipSuccess; ++v) {
+    const Kernels K = kernels_for(cfg->dtype, (v & 1) == 1, h->nper);
+    const void* fn = (const void*)(v < 2 ? K.stream : K.stream_t);
     hipFuncAttributes fa;
     e = hipFuncGetAttributes(&fa, fn);
     if (e == hipSuccess && fa.localSizeBytes > 0) e = hipErrorInvalidConfiguration;
+    if (v >= 2) continue;
+    int per_cu = 0;
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStreamThreads, 0);
     h->cap[v] = cus * per_cu;
+    if (h->cap[v] > capmax) capmax = h->cap[v];
     if (e == hipSuccess && (h->cap[v] / kGroups) * kStreamWaves < C) e = hipErrorInvalidConfiguration;
   }
   const size_t n1 = (size_t)rows * C * kX1 * sizeof(uint64_t);
-  const int capmax = h->cap[0] > h->cap[1] ? h->cap[0] : h->cap[1];
   const size_t nd = (size_t)capmax * kStreamWaves * 8 * sizeof(uint64_t);   // dummy slots, per stream wave
   const size_t n2 = (size_t)rows * C * kPart * sizeof(float);
   const size_t n3 = (size_t)rows * sizeof(int4);
@@ -1389,11 +1427,12 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
                    (!has_dl || (!((uintptr_t)in->draft_logits & 15) && !((in->draft_stride * esize) & 15)));
 
   // Persistent grid: per row group, as many waves as the device holds, never
-  // more than the busiest group has items.
+  // more than the busiest group has items.  Without draft logits: one wave
+  // per item.
   const int C = h->chunks;
   const int64_t items_g = ((R_t + kGroups - 1) / kGroups) * C;
-  int64_t wg = h->cap[vec ? 1 : 0] / kGroups;
   const int64_t need = (items_g + kStreamWaves - 1) / kStreamWaves;
+  int64_t wg = has_dl ? h->cap[vec ? 1 : 0] / kGroups : need;
   if (wg > need) wg = need;
   if (wg < 1) wg = 1;
   const int gmax = in->cu_draft == nullptr ? in->gamma : h->cfg.max_gamma;
@@ -1445,7 +1484,7 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   if (h->timing && h->trec < SPECVERIFY_TIMING_RUNS) ev = h->ev + 3 * h->trec++;
   if (ev) e = hipEventRecord(ev[0], stream);
   if (in->cu_draft) hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, P, h->rowinfo, h->layout);
-  hipLaunchKernelGGL(K.stream, dim3((uint32_t)(wg * kGroups)), dim3(kStreamThreads), 0, stream, P);
+  hipLaunchKernelGGL(has_dl ? K.stream : K.stream_t, dim3((uint32_t)(wg * kGroups)), dim3(kStreamThreads), 0, stream, P);
   if (ev && e == hipSuccess) e = hipEventRecord(ev[1], stream);
   hipLaunchKernelGGL(K.finish, dim3(B), dim3(64 * fwaves), 0, stream, P);
   if (ev && e == hipSuccess) e = hipEventRecord(ev[2], stream);
