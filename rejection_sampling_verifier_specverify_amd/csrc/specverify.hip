@@ -909,10 +909,34 @@ __device__ __forceinline__ float load_logit(const char* base, int64_t row, int64
   return __uint_as_float((uint32_t)((const uint16_t*)p)[t] << 16);
 }
 
+// What a row's resolution reads first: its chunk slots, its partials and
+// the drafted token.  finish_kernel issues these before the row's
+// temperature is known, so that their latency overlaps the scalar loads.
+template <int NPER>
+struct RowIn {
+  RowSlots<NPER> q;
+  float4 pt[NPER];   // {tag, W_c, B_c} of the lane's chunks (rows with draft logits)
+  int x;             // drafted token (rows with a draft)
+};
+template <int NPER>
+__device__ __forceinline__ void row_loads(const Params& P, int r, int rd, bool pair, int lane, RowIn<NPER>& in) {
+  uint32_t soff[NPER];
+  slot_offsets(P.C, lane, soff);
+  slots_issue(P, r, true, soff, in.q);
+  const bool dp = pair && !P.token_only;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const int c = lane + 64 * j;
+    in.pt[j] = (dp && c < P.C) ? *(const float4*)(P.part + ((int64_t)r * P.C + c) * kPart)
+                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  in.x = pair ? ld_const(P.tokens, rd) : 0;
+}
+
 // One row of a sampled sequence, on one wave.  Returns the row result.
 template <int DT, bool VEC, int NPER>
 __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int rd, bool pair, float T, float ui,
-                                                   float ug, int lane) {
+                                                   float ug, int lane, const RowIn<NPER>& in) {
   using F = Fmt<DT>;
   const int C = P.C;
   const uint32_t tag = P.epoch;
@@ -920,24 +944,19 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
   const float ninf = -__builtin_huge_valf();
   // dp: the draft's logits are there; tk: a token-only draft, q = delta_x
   const bool dp = pair && !P.token_only, tk = pair && P.token_only;
-  const int x = pair ? ld_const(P.tokens, rd) : 0;
+  const int x = in.x;
   const bool x_ok = x >= 0 && x < P.V;
-  RowSlots<NPER> q;
-  uint32_t soff[NPER];
-  slot_offsets(C, lane, soff);
-  slots_issue(P, r, true, soff, q);
+  const RowSlots<NPER>& q = in.q;
   float W[NPER], Bp[NPER];
   int done = 1;
 #pragma unroll
   for (int j = 0; j < NPER; ++j) {
     W[j] = 0.0f;
     Bp[j] = 0.0f;
-    const int c = lane + 64 * j;
-    if (dp && c < C) {
-      const float4 pt = *(const float4*)(P.part + ((int64_t)r * C + c) * kPart);
-      done &= __float_as_uint(pt.x) == tag;
-      W[j] = pt.y;
-      Bp[j] = pt.z;
+    if (dp && lane + 64 * j < C) {
+      done &= __float_as_uint(in.pt[j].x) == tag;
+      W[j] = in.pt[j].y;
+      Bp[j] = in.pt[j].z;
     }
   }
   float lx = 0.0f, dx = 0.0f;
@@ -987,22 +1006,6 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
     Z = wave_sum(zl);
     beta = wave_sum(bl);
   }
-  // p(x), q(x): the logits at x with their chunk's offset and scale; the
-  // acceptance test u q(x) < p(x)
-  if (pair) {
-    const float mdx = lane_f(pick(md, jx), lxl);
-    const float px = chunk_scale(mtx, Mt, St, s) * ex;
-    const float qx = tk ? 1.0f : chunk_scale(mdx, Md, Sd, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(dx, s, chunk_offset(mdx, s)));
-    if (tk) beta = px;   // sum min(p, delta_x) = p(x)
-    if (lane == 0) {
-      if (P.p_draft) P.p_draft[rd] = px;
-      if (P.q_draft) P.q_draft[rd] = qx;
-      if (P.beta) P.beta[rd] = beta;
-      if (P.resid) P.resid[rd] = Z;
-    }
-    // an accepted draft emits itself: its row's residual token is never used
-    if (ui * qx < px) return row_payload(0, true, 0);
-  }
   const bool resid = pair && Z > 0.0f;
   float ml = 0.0f;
 #pragma unroll
@@ -1041,7 +1044,8 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
     cs = last;
     before = last_before;
   }
-  if (cs < 0) return row_payload(2, false, 0);   // unreachable for a valid row
+  const bool no_owner = cs < 0;   // unreachable for a valid row
+  if (no_owner) cs = 0;
   const int ls = cs & 63, js = cs >> 6;
   const float a_s = lane_f(pick(at, js), ls);
   const float rho_s = lane_f(pick(rho, js), ls);
@@ -1053,23 +1057,55 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
   issue_row<DT, VEC>(row_rsrc(P.target, r, P.tstride_b, nb), cs, lane, R[0]);
   const bool rd_read = resid && dp;
   issue_row<DT, VEC>(row_rsrc(P.draft, rd_read ? rd : 0, P.dstride_b, rd_read ? nb : 0), cs, lane, R[1]);
+  // The owner chunk needs only the slots and partials (and, for a token-only
+  // draft, x's logit): its loads go out before the acceptance test, whose
+  // logits at x may still be in flight.
+  // p(x), q(x): the logits at x with their chunk's offset and scale; the
+  // acceptance test u q(x) < p(x)
+  if (pair) {
+    const float mdx = lane_f(pick(md, jx), lxl);
+    const float px = chunk_scale(mtx, Mt, St, s) * ex;
+    const float qx = tk ? 1.0f : chunk_scale(mdx, Md, Sd, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(dx, s, chunk_offset(mdx, s)));
+    if (tk) beta = px;   // sum min(p, delta_x) = p(x)
+    if (lane == 0) {
+      if (P.p_draft) P.p_draft[rd] = px;
+      if (P.q_draft) P.q_draft[rd] = qx;
+      if (P.beta) P.beta[rd] = beta;
+      if (P.resid) P.resid[rd] = Z;
+    }
+    // an accepted draft emits itself: its row's residual token is never used
+    // (the owner chunk's loads land before the wave goes on)
+    if (ui * qx < px) {
+      __builtin_amdgcn_s_waitcnt(0);
+      return row_payload(0, true, 0);
+    }
+  }
+  if (no_owner) return row_payload(2, false, 0);
   float w[F::L], ld[F::L];
   unpack<DT>(R[0], w);
   unpack<DT>(R[1], ld);
   if ((cs + 1) * F::CH > P.V) mask_tail2<DT>(w, ld, cs, P.V, lane);
+  // one branch per row, straight-line loops (independent chains per element)
+  if (tk && resid) {
 #pragma unroll
-  for (int k = 0; k < F::L; ++k) {
-    const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(w[k], s, ct));
-    if (tk && resid)
-      w[k] = token_of<DT>(cs, k, lane) == x ? 0.0f : et;   // p without x
-    else
-      w[k] = resid ? resid_w(et, __builtin_amdgcn_exp2f(__builtin_fmaf(ld[k], s, cd)), rho_s) : et;
+    for (int k = 0; k < F::L; ++k) {   // p without x
+      const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(w[k], s, ct));
+      w[k] = token_of<DT>(cs, k, lane) == x ? 0.0f : et;
+    }
+  } else if (resid) {
+#pragma unroll
+    for (int k = 0; k < F::L; ++k)
+      w[k] = resid_w(__builtin_amdgcn_exp2f(__builtin_fmaf(w[k], s, ct)),
+                     __builtin_amdgcn_exp2f(__builtin_fmaf(ld[k], s, cd)), rho_s);
+  } else {
+#pragma unroll
+    for (int k = 0; k < F::L; ++k) w[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(w[k], s, ct));
   }
   // Running sums in the chunk's units against tau = (thr - before) / a_s.
   // Token order inside the chunk is round u, then lane, then element: a
   // wave scan of the lane sums per round, rounds in order.
   const float tau = (thr - before) / a_s;
-  int first = 0x7FFFFFFF, lastpos = -1;
+  int first = 0x7FFFFFFF, lastpos = -1;   // per lane until the reductions below
   float rbase = 0.0f;
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
@@ -1091,10 +1127,10 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
         lastpos = max(lastpos, k);
       }
     }
-    cand = wave_min_i(cand);
-    if (first == 0x7FFFFFFF) first = cand;   // an earlier round's hit wins
+    first = min(first, cand);   // positions grow with the round: the least hit is the first
     rbase = rbase + lane_f(incl, 63);
   }
+  first = wave_min_i(first);
   lastpos = wave_max_i(lastpos);
   const int pickk = first != 0x7FFFFFFF ? first : lastpos;
   if (pickk < 0) return row_payload(2, false, 0);   // unreachable: the chunk has weight > 0
@@ -1105,15 +1141,13 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
 
 // One row of a greedy sequence, on one wave.
 template <int NPER>
-__device__ __forceinline__ uint32_t finish_greedy(const Params& P, int r, int rd, bool pair, int lane) {
+__device__ __forceinline__ uint32_t finish_greedy(const Params& P, int r, int rd, bool pair, int lane,
+                                                  const RowIn<NPER>& in) {
   const int C = P.C;
   const uint32_t tag = P.epoch;
   // dp: the draft's logits are there; a token-only draft's argmax is x itself
   const bool dp = pair && !P.token_only;
-  RowSlots<NPER> q;
-  uint32_t soff[NPER];
-  slot_offsets(C, lane, soff);
-  slots_issue(P, r, true, soff, q);
+  const RowSlots<NPER>& q = in.q;
   if (!slots_ready(q, C, tag, dp ? 4 : 2, lane)) return row_payload(2, false, 0);
   float av = -__builtin_huge_valf(), dv = -__builtin_huge_valf();
   int ak = 0x7FFFFFFF, dk = 0x7FFFFFFF, bad = 0;
@@ -1135,7 +1169,7 @@ __device__ __forceinline__ uint32_t finish_greedy(const Params& P, int r, int rd
     return row_payload(1, false, 0);
   bool acc = false;
   if (pair) {
-    const int x = ld_const(P.tokens, rd);
+    const int x = in.x;
     if (x < 0 || x >= P.V) return row_payload(1, false, 0);
     if (!dp) dk = x;
     acc = (x == ak);
@@ -1153,7 +1187,8 @@ template <int DT, bool VEC, int NPER>
 __global__ __launch_bounds__(64 * kFinishWaves) void finish_kernel(Params P) {
   __shared__ FinishShared sh;
   const int b = blockIdx.x;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // rows are wave-uniform
   const int nw = blockDim.x >> 6;
   int d0, gam;
   if (P.cu_draft == nullptr) {
@@ -1176,10 +1211,12 @@ __global__ __launch_bounds__(64 * kFinishWaves) void finish_kernel(Params P) {
   for (int j = wv; j <= gam; j += nw) {
     const bool pair = j < gam;
     const int r = t0 + j, rd = d0 + j;
+    RowIn<NPER> in;
+    row_loads(P, r, rd, pair, lane, in);
     uint32_t res;
     if (!t_ok) res = row_payload(1, false, 0);
-    else if (sampled) res = finish_sampled<DT, VEC, NPER>(P, r, rd, pair, T, ld_const(P.uniforms, r), ug, lane);
-    else res = finish_greedy<NPER>(P, r, rd, pair, lane);
+    else if (sampled) res = finish_sampled<DT, VEC, NPER>(P, r, rd, pair, T, ld_const(P.uniforms, r), ug, lane, in);
+    else res = finish_greedy<NPER>(P, r, rd, pair, lane, in);
     if (lane == 0) sh.res[j] = res;
   }
   __syncthreads();
