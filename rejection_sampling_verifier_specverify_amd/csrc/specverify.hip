@@ -797,7 +797,12 @@ __device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy
                                      const Item& cur, const float (&Ecur)[2][Fmt<DT>::L], float cmt, float cmd,
                                      float cst, const Item& n1, u32x4 (&R1)[2][kU], float (&Efree)[2][Fmt<DT>::L],
                                      float& nmt, float& nmd, float& nst, const Item& n3) {
+  // Phase 1 publishes what other waves' phase 2 polls for: it runs at a
+  // higher issue priority than the other wave of its SIMD (1.2 us faster per
+  // launch than equal priorities).
+  __builtin_amdgcn_s_setprio(3);
   p1_item<DT>(P, n1, lane, wdummy, R1, Efree, nmt, nmd, nst);
+  __builtin_amdgcn_s_setprio(0);
   slots_issue(P, cur.r(), cur.mode() == 1 && cur.pair(), soff, q);
   const bool ready = slots_ready(q, P.C, P.epoch, kX1, lane);   // consumes the poll on every path
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
