@@ -1082,7 +1082,7 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
     // (the owner chunk's loads land before the wave goes on)
     if (ui * qx < px) {
       __builtin_amdgcn_s_waitcnt(0);
-      return row_payload(0, true, 0);
+      return row_payload(0, true, x);   // an accepted row emits its draft
     }
   }
   if (no_owner) return row_payload(2, false, 0);
@@ -1235,14 +1235,11 @@ __global__ __launch_bounds__(64 * kFinishWaves) void finish_kernel(Params P) {
     const uint64_t rb = __ballot(j < gam && !(v & kAccBit));
     if (n == gam && rb) n = j0 + __builtin_ctzll(rb);
   }
-  const int tn = (int)(sh.res[n] & kTokMask);
+  // rows up to n carry their emitted token: the draft when accepted, the
+  // residual or bonus token at n
   for (int j0 = 0; j0 <= gam; j0 += 64) {
     const int j = j0 + lane;
-    if (j <= gam) {
-      int o = -1;
-      if (st == 0) o = (j < n) ? P.tokens[d0 + j] : (j == n ? tn : -1);
-      P.out_tokens[t0 + j] = o;
-    }
+    if (j <= gam) P.out_tokens[t0 + j] = (st == 0 && j <= n) ? (int)(sh.res[j] & kTokMask) : -1;
   }
   if (lane == 0) P.acc_len[b] = st == 2 ? -2 : st == 1 ? -1 : n;
 }
