@@ -396,3 +396,64 @@ def test_token_only_one_poll_budget_bit_exact():
         assert np.array_equal(ga[k], gb[k], equal_nan=True), k
     rep = compare(inp, ga)
     assert rep.ok(), rep.summary()
+
+
+@pytest.mark.parametrize("case", ["nan", "all_neginf", "token", "neg_T", "nan_T", "tiny_T", "nan_greedy",
+                                  "partial_neginf"])
+def test_token_only_invalid_data_flagged_per_sequence(case):
+    """The phase-1-only launch (no draft logits) flags the same invalid data."""
+    rng = np.random.default_rng(16)
+    V, gam = 10000, [2, 2, 2]
+    tgt = rng.normal(size=(9, V))
+    toks = rng.integers(0, V, 6).astype(np.int32)
+    T = [1.0, 1.0, 0.0]
+    bad = 1
+    if case == "nan":
+        tgt[5, 9999] = np.nan          # bonus row of sequence 1
+    elif case == "all_neginf":
+        tgt[4, :] = -np.inf
+    elif case == "token":
+        toks[3] = V
+    elif case == "neg_T":
+        T[1] = -1.0
+    elif case == "nan_T":
+        T[1] = float("nan")
+    elif case == "tiny_T":
+        T[1] = 1e-39
+    elif case == "nan_greedy":
+        tgt[7, 123] = np.nan           # sequence 2 is greedy
+        bad = 2
+    elif case == "partial_neginf":
+        tgt[3:6, : V // 2] = -np.inf   # valid: only half the row
+    drf = rng.normal(size=(6, V))
+    inp = token_only(make_custom(tgt, drf, toks, rng.random(9), T, gam, dtype="f32"))
+    rep, got = _check(inp, label=f"token-only invalid {case}")
+    if case == "partial_neginf":
+        assert np.all(got["accepted_len"] >= 0)
+    else:
+        assert rep.invalid == 1
+        assert got["accepted_len"][bad] == -1
+        assert np.all(got["out_tokens"][bad * 3: bad * 3 + 3] == -1)
+
+
+def test_token_only_invalid_layout_flags_whole_batch():
+    import torch
+    inp = token_only(_rand_custom(5000, [2, 3, 1, 2], [1.0] * 4, seed=12))
+    sv = _handle(inp)
+    dev = to_device(inp)
+    cu = inp.cu_draft.astype(np.int32).copy()
+    cu[2] = cu[1] - 1
+    out = alloc_outputs(inp)
+    gpu_run(sv, dict(dev, cu_draft=torch.from_numpy(cu).to("cuda:0")), out, inp, ragged=True)
+    got = fetch(out)
+    assert np.all(got["accepted_len"] == -1) and np.all(got["out_tokens"] == -1)
+    out2 = alloc_outputs(inp)
+    gpu_run(sv, dev, out2, inp, ragged=True)
+    assert compare(inp, fetch(out2)).ok()
+
+
+def test_ragged_all_gamma_zero_runs_phase_one_only():
+    """A ragged batch with no drafts at all (R_d = 0): plain sampling of every row."""
+    inp = _rand_custom(40000, [0] * 9, [0.7, 1.0, 0.0, 0.5, 1.3, 0.0, 0.9, 1.0, 0.2], seed=13)
+    rep, _ = _check(inp, ragged=True, label="ragged gamma=0")
+    assert rep.checked == 9
