@@ -237,11 +237,12 @@ __device__ __forceinline__ int wave_max_i(int v) {
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 // (value, index): larger value wins, lower index on ties.
+// (v2, k2) wins over (v, k) if larger, or equal with a lower index.  Written
+// without short-circuit evaluation: selects, not branches.
 __device__ __forceinline__ void argmax_merge(float& v, int& k, float v2, int k2) {
-  if (v2 > v || (v2 == v && k2 < k)) {
-    v = v2;
-    k = k2;
-  }
+  const bool take = (v2 > v) | ((v2 == v) & (k2 < k));
+  v = take ? v2 : v;
+  k = take ? k2 : k;
 }
 template <int CTRL>
 __device__ __forceinline__ void argmax_step(float& v, int& k) {
