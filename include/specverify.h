@@ -129,8 +129,9 @@ typedef struct {
 
 /* Allocate a handle and its workspace on cfg->device.  On failure *out is
  * NULL.  Errors: INVALID_ARGUMENT (NULL or out-of-range config),
- * UNSUPPORTED (vocab too large), DEVICE (no such device / runtime error),
- * OUT_OF_MEMORY. */
+ * UNSUPPORTED (vocab too large; or a library build whose kernels would
+ * spill registers to scratch memory, which is refused rather than run),
+ * DEVICE (no such device / runtime error), OUT_OF_MEMORY. */
 specverify_status specverify_create(const specverify_config* cfg, specverify_handle* out);
 
 /* Verify one batch, asynchronously on hip_stream (a hipStream_t; NULL = the

@@ -662,11 +662,13 @@ __device__ __forceinline__ void greedy_row(const float (&x)[Fmt<DT>::L], int c, 
 // later (rows that were not read hold zeros).  Likewise every path ends in
 // the same one store (items with nothing to publish write the dummy slots),
 // so the count of memory operations in flight is the same on all paths.
-// D false: the launch has no draft logits; only row 0 exists.
+// D false: the launch has no draft logits; only row 0 exists.  `x` (D
+// false, sampled rows): a drafted token; if this chunk holds it, slot 2
+// carries e_t at x instead of the absent draft's maximum.
 template <int DT, bool D = true>
 __device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lane, uint64_t* wdummy,
                                         const u32x4 (&R)[2][kU], float (&E)[2][Fmt<DT>::L], float& mt,
-                                        float& md, float& st) {
+                                        float& md, float& st, int x = -1) {
   unpack<DT>(R[0], E[0]);
   if (D) unpack<DT>(R[1], E[1]);
   uint32_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
@@ -683,6 +685,15 @@ __device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lan
       v1 = __float_as_uint(st);
       v2 = __float_as_uint(md);
       v3 = __float_as_uint(sd);
+      const int t = x - it.c() * Fmt<DT>::CH;   // x's position in the chunk
+      if (!D && x >= 0 && x < P.V && t >= 0 && t < Fmt<DT>::CH) {
+        using F = Fmt<DT>;
+        const int k = (t / (64 * F::EPV)) * F::EPV + t % F::EPV;   // element of lane (t / EPV) % 64
+        float ex = 0.0f;
+#pragma unroll
+        for (int i = 0; i < F::L; ++i) ex = i == k ? E[0][i] : ex;
+        v2 = __float_as_uint(lane_f(ex, (t / F::EPV) & 63));
+      }
     } else {
       float vt, vd = -__builtin_huge_valf();
       int kt, kd = 0x7FFFFFFF, bt, bd = 0;
@@ -883,8 +894,16 @@ __global__ __launch_bounds__(kStreamThreads) void stream_t_kernel(Params P) {
   u32x4 R[2][kU];               // row 1 is never loaded or read
   float E[2][F::L];
   issue_target<DT, VEC>(P, it, lane, R[0]);
+  // a token-only draft x of this row: the chunk that holds it also publishes
+  // e_t at x (slot 2, unused without draft logits), so that the finish needs
+  // no dependent read of the logit at x
+  int x = -1;
+  if (P.token_only && it.mode() == 1) {
+    const RowMeta m = row_meta(P, it.r());
+    if (m.pair) x = ld_const(P.tokens, m.rd);
+  }
   float mt, md, st;
-  p1_item<DT, false>(P, it, lane, P.dummy, R, E, mt, md, st);
+  p1_item<DT, false>(P, it, lane, P.dummy, R, E, mt, md, st, x);
 }
 
 // ================================================================== finish kernel
@@ -966,9 +985,9 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
     }
   }
   float lx = 0.0f, dx = 0.0f;
-  if (pair && x_ok) {
+  if (dp && x_ok) {   // token-only rows read e_t at x from the slots instead
     lx = load_logit<DT>(P.target, r, P.tstride_b, x);
-    if (dp) dx = load_logit<DT>(P.draft, rd, P.dstride_b, x);
+    dx = load_logit<DT>(P.draft, rd, P.dstride_b, x);
   }
   if (!slots_ready(q, C, tag, dp ? 4 : 2, lane) || !__all(done)) return row_payload(2, false, 0);
   float Mt, St, Md = ninf, Sd = 0.0f;
@@ -988,8 +1007,23 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
     rho[j] = (in && dp) ? chunk_rho(mt[j], Mt, St, md[j], Md, Sd, s) : 0.0f;
   }
   const float mtx = lane_f(pick(mt, jx), lxl);
-  // e at x as phase 1 computed it (the same operations on the same values)
-  const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(lx, s, chunk_offset(mtx, s)));
+  // e at x as phase 1 computed it (the same operations on the same values);
+  // for a token-only draft phase 1 published it in slot 2 of x's chunk
+  float ex;
+  if (tk) {
+    uint32_t tgx = 0, vx = 0;   // slot 2 of chunk cx, read from its lane
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      const uint32_t tj = (uint32_t)__builtin_amdgcn_readlane((int)slot_tag(q.w[j][2]), lxl);
+      const uint32_t vj = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)q.w[j][2], lxl);
+      tgx = j == jx ? tj : tgx;
+      vx = j == jx ? vj : vx;
+    }
+    if (tgx != tag) return row_payload(2, false, 0);   // not published: internal error
+    ex = __uint_as_float(vx);
+  } else {
+    ex = __builtin_amdgcn_exp2f(__builtin_fmaf(lx, s, chunk_offset(mtx, s)));
+  }
   if (tk) {
     // the residual p - delta_x is p without x: the chunk sums of e_t, less
     // x's own e in its chunk
@@ -1382,14 +1416,14 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
   int cus = 0;
   h->cap[0] = h->cap[1] = 0;
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cfg->device);
-  // A stream kernel that spilled to scratch would make the runtime allocate
-  // scratch at its first launch and spill in its inner loop: such a build is
-  // refused rather than run.  (The kernel without draft logits never waits
+  // A kernel that spilled to scratch would make the runtime allocate scratch
+  // at its first launch and spill in its inner loop: such a build is refused
+  // rather than run.  (The kernel without draft logits never waits
   // on other waves: its grid is not persistent and needs no residency.)
   int capmax = 0;
-  for (int v = 0; v < 4 && e == hipSuccess; ++v) {
+  for (int v = 0; v < 6 && e == hipSuccess; ++v) {
     const Kernels K = kernels_for(cfg->dtype, (v & 1) == 1, h->nper);
-    const void* fn = (const void*)(v < 2 ? K.stream : K.stream_t);
+    const void* fn = (const void*)(v < 2 ? K.stream : v < 4 ? K.stream_t : K.finish);
     hipFuncAttributes fa;
     e = hipFuncGetAttributes(&fa, fn);
     if (e == hipSuccess && fa.localSizeBytes > 0) e = hipErrorInvalidConfiguration;
