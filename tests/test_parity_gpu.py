@@ -457,3 +457,18 @@ def test_ragged_all_gamma_zero_runs_phase_one_only():
     inp = _rand_custom(40000, [0] * 9, [0.7, 1.0, 0.0, 0.5, 1.3, 0.0, 0.9, 1.0, 0.2], seed=13)
     rep, _ = _check(inp, ragged=True, label="ragged gamma=0")
     assert rep.checked == 9
+
+
+def test_token_only_headline_full_size_every_sequence():
+    """The benchmarked batch with token-only drafts (the bench line's token_only run), all 64 sequences."""
+    inp = token_only(make_inputs("b64_g4_v128256_bf16", seed=0))
+    rep, _ = _check(inp, label="token-only headline full")
+    assert rep.checked == 64
+
+
+@pytest.mark.parametrize("name", ["b256_g8_v128256_bf16_mixedT", "b512_gragged1to7_v152064_bf16"])
+def test_token_only_large_full_size_sampled_sequences(name):
+    inp = token_only(make_inputs(name, seed=0))
+    B = inp.batch
+    seqs = sorted(set(np.linspace(0, B - 1, 20).astype(int).tolist()) | {0, B - 1})
+    _check(inp, sequences=seqs, label=f"token-only {name} full (sampled {len(seqs)})")
