@@ -38,13 +38,23 @@
 // without a draft gets a zero-sized buffer, so every item issues the same
 // loads and none of them touches memory it should not.
 //
+// stream_t_kernel replaces stream_kernel when a run has no draft logits
+// (token-only drafts, q = delta_x; or no drafts at all): phase 1 only, one
+// item per wave, no exchange.  The chunk that holds a drafted token x also
+// publishes e_t at x.
+//
 // finish_kernel, one workgroup per sequence and one wave per row, then
-// merges the partials: Z and beta; p(x) and q(x) from the two logits of the
-// drafted token; the chunk whose CDF interval holds u_gamma * Z (or the CDF
-// of p for the bonus row and when Z = 0), whose logits it re-reads and scans
-// in token order for the token; the acceptance test u_i q(x) < p(x);
-// finally the sequence's first rejection n, accepted_len and the n + 1
-// tokens.  The accepted length never leaves the device.
+// merges the partials: Z and beta; the chunk whose CDF interval holds
+// u_gamma * Z (or the CDF of p for the bonus row and when Z = 0), whose
+// logits it re-reads; p(x) and q(x) from the two logits of the drafted token
+// (a token-only draft: e_t at x from the slots, q(x) = 1); the acceptance
+// test u_i q(x) < p(x); for a rejected row, the scan of the re-read chunk
+// in token order for the token; finally the sequence's first rejection n,
+// accepted_len and the n + 1 tokens.  The accepted length never leaves the
+// device.
+//
+// commit_kernel (its own call, specverify_commit) appends each sequence's
+// n + 1 emitted tokens to its token row on the device.
 //
 // Inside stream_kernel, values cross waves only in 64-bit slots that carry a
 // 32-bit epoch tag next to the value.  A slot is written with one aligned
