@@ -226,8 +226,13 @@ __device__ __forceinline__ float wave_scan(float v, int lane) {
   v += dpp<0x114>(v);   // row_shr:4
   v += dpp<0x118>(v);   // row_shr:8
   const float t0 = lane_f(v, 15), t1 = lane_f(v, 31), t2 = lane_f(v, 47);
+  const float t01 = t0 + t1, t012 = t01 + t2;
+  // the offset of the lane's row of 16, by selects (a chained conditional
+  // here compiled to branches on the lane)
   const int row = lane >> 4;
-  const float off = row == 0 ? 0.0f : row == 1 ? t0 : row == 2 ? (t0 + t1) : ((t0 + t1) + t2);
+  float off = row >= 1 ? t0 : 0.0f;
+  off = row >= 2 ? t01 : off;
+  off = row >= 3 ? t012 : off;
   return v + off;
 }
 __device__ __forceinline__ int wave_min_i(int v) {
