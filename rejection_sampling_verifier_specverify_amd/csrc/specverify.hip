@@ -470,6 +470,35 @@ __device__ __forceinline__ float elem(const u32x4& w, int e, int lim) {
   return e >= lim ? -__builtin_huge_valf() : x;
 }
 
+// Element e of a lane's 16-byte vector w, as unpack leaves it.
+template <int DT>
+__device__ __forceinline__ float vec_elem(const u32x4& w, int e) {
+  if (DT == SPECVERIFY_F32) return __uint_as_float(w[e]);
+  const uint32_t h = w[e >> 1];
+  return __uint_as_float((e & 1) ? (h & 0xFFFF0000u) : (h << 16));
+}
+// Tokens >= V of the last chunk become -inf in the raw words of a row (one
+// comparison per token, as in mask_tail2).
+template <int DT>
+__device__ __forceinline__ void mask_raw(u32x4 (&raw)[kU], int c, int V, int lane) {
+  using F = Fmt<DT>;
+  const int lim = V - (c * F::CH + lane * F::EPV);
+#pragma unroll
+  for (int u = 0; u < kU; ++u)
+#pragma unroll
+    for (int e = 0; e < F::EPV; ++e) {
+      const bool out = u * 64 * F::EPV + e >= lim;
+      if (DT == SPECVERIFY_F32) {
+        raw[u][e] = out ? 0xFF800000u : raw[u][e];
+      } else {
+        const uint32_t w = raw[u][e >> 1];
+        const uint32_t m = (e & 1) ? ((w & 0x0000FFFFu) | 0xFF800000u) : ((w & 0xFFFF0000u) | 0x0000FF80u);
+        raw[u][e >> 1] = out ? m : w;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // ------------------------------------------------------------------ sequence layout
 
 // Read-only inputs that a wave reads at a uniform address go through the
@@ -1136,39 +1165,49 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
     }
   }
   if (no_owner) return row_payload(2, false, 0);
-  float w[F::L], ld[F::L];
-  unpack<DT>(R[0], w);
-  unpack<DT>(R[1], ld);
-  if ((cs + 1) * F::CH > P.V) mask_tail2<DT>(w, ld, cs, P.V, lane);
-  // one branch per row, straight-line loops (independent chains per element)
-  if (tk && resid) {
-#pragma unroll
-    for (int k = 0; k < F::L; ++k) {   // p without x
-      const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(w[k], s, ct));
-      w[k] = token_of<DT>(cs, k, lane) == x ? 0.0f : et;
-    }
-  } else if (resid) {
-#pragma unroll
-    for (int k = 0; k < F::L; ++k)
-      w[k] = resid_w(__builtin_amdgcn_exp2f(__builtin_fmaf(w[k], s, ct)),
-                     __builtin_amdgcn_exp2f(__builtin_fmaf(ld[k], s, cd)), rho_s);
-  } else {
-#pragma unroll
-    for (int k = 0; k < F::L; ++k) w[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(w[k], s, ct));
+  if ((cs + 1) * F::CH > P.V) {   // tokens >= V: weight 0
+    mask_raw<DT>(R[0], cs, P.V, lane);
+    mask_raw<DT>(R[1], cs, P.V, lane);
   }
   // Running sums in the chunk's units against tau = (thr - before) / a_s.
-  // Token order inside the chunk is round u, then lane, then element: a
-  // wave scan of the lane sums per round, rounds in order.
+  // Token order inside the chunk is round u (one 16-byte vector per lane),
+  // then lane, then element.  Per round: the weights (recomputed with the
+  // same functions as phase 2, one branch per row around straight-line
+  // code), a wave scan of the lane sums and the first position whose running
+  // sum exceeds tau.  Rounds go in order and stop at the first with a hit.
   const float tau = (thr - before) / a_s;
-  int first = 0x7FFFFFFF, lastpos = -1;   // per lane until the reductions below
+  int first = 0x7FFFFFFF, lastpos = -1;
   float rbase = 0.0f;
-#pragma unroll
+#pragma unroll 1
   for (int u = 0; u < kU; ++u) {
+    // the round's two vectors, picked by selects (u is wave-uniform)
+    u32x4 vt = R[0][0], vd = R[1][0];
+#pragma unroll
+    for (int i = 1; i < kU; ++i) {
+      vt = i == u ? R[0][i] : vt;
+      vd = i == u ? R[1][i] : vd;
+    }
+    float w[F::EPV];
+    if (tk && resid) {
+#pragma unroll
+      for (int e = 0; e < F::EPV; ++e) {   // p without x
+        const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vt, e), s, ct));
+        w[e] = token_of<DT>(cs, u * F::EPV + e, lane) == x ? 0.0f : et;
+      }
+    } else if (resid) {
+#pragma unroll
+      for (int e = 0; e < F::EPV; ++e)
+        w[e] = resid_w(__builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vt, e), s, ct)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vd, e), s, cd)), rho_s);
+    } else {
+#pragma unroll
+      for (int e = 0; e < F::EPV; ++e) w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vt, e), s, ct));
+    }
     float loc[F::EPV];
     float run = 0.0f;
 #pragma unroll
     for (int e = 0; e < F::EPV; ++e) {
-      run += w[u * F::EPV + e];
+      run += w[e];
       loc[e] = run;
     }
     const float incl = wave_scan(run, lane);
@@ -1177,16 +1216,18 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
 #pragma unroll
     for (int e = F::EPV - 1; e >= 0; --e) {
       const int k = u * 64 * F::EPV + lane * F::EPV + e;   // position inside the chunk
-      if (w[u * F::EPV + e] > 0.0f) {
+      if (w[e] > 0.0f) {
         if (excl + loc[e] > tau) cand = k;
         lastpos = max(lastpos, k);
       }
     }
-    first = min(first, cand);   // positions grow with the round: the least hit is the first
+    if (__ballot(cand != 0x7FFFFFFF)) {   // positions grow with the round: this round's least hit is the first
+      first = wave_min_i(cand);
+      break;
+    }
     rbase = rbase + lane_f(incl, 63);
   }
-  first = wave_min_i(first);
-  lastpos = wave_max_i(lastpos);
+  if (first == 0x7FFFFFFF) lastpos = wave_max_i(lastpos);   // every round was scanned
   const int pickk = first != 0x7FFFFFFF ? first : lastpos;
   if (pickk < 0) return row_payload(2, false, 0);   // unreachable: the chunk has weight > 0
   const int tok = cs * F::CH + pickk;
