@@ -749,10 +749,10 @@ __device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lan
       v3 = bd ? 0xFFFFFFFFu : (uint32_t)kd;
     }
   }
-  if (lane < kX1) {
-    const uint32_t v = lane == 0 ? v0 : lane == 1 ? v1 : lane == 2 ? v2 : v3;
-    slot_put(dst + lane, P.epoch, v);
-  }
+  uint32_t v = lane == 2 ? v2 : v3;   // selects, not a chain of branches on the lane
+  v = lane == 1 ? v1 : v;
+  v = lane == 0 ? v0 : v;
+  if (lane < kX1) slot_put(dst + lane, P.epoch, v);
 }
 
 // A wave that has polled long enough for the slots of its row computes the
@@ -786,7 +786,9 @@ __device__ __forceinline__ void help_row(const Params& P, const Item& it, int la
       stats_mem<DT, VEC>(rt, c, P.V, lane, it.s, mt, st);
       stats_mem<DT, VEC>(rd, c, P.V, lane, it.s, md, sd);
       if (lane < kX1) {
-        const uint32_t x = __float_as_uint(lane == 0 ? mt : lane == 1 ? st : lane == 2 ? md : sd);
+        float y = lane == 2 ? md : sd;
+        y = lane == 1 ? st : y;
+        const uint32_t x = __float_as_uint(lane == 0 ? mt : y);
         slot_put(P.xch1 + ((int64_t)it.r() * P.C + c) * kX1 + lane, tag, x);
       }
     }
