@@ -472,3 +472,50 @@ def test_token_only_large_full_size_sampled_sequences(name):
     B = inp.batch
     seqs = sorted(set(np.linspace(0, B - 1, 20).astype(int).tolist()) | {0, B - 1})
     _check(inp, sequences=seqs, label=f"token-only {name} full (sampled {len(seqs)})")
+
+
+def _as_f64(logits, dtype):
+    a = np.asarray(logits)
+    if dtype == "bf16":
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+@pytest.mark.parametrize("tok", [False, True])
+@pytest.mark.parametrize("ug", [0.0, float(np.nextafter(np.float32(1.0), np.float32(0.0)))])
+def test_final_uniform_extremes_emit_tokens_with_weight(ug, tok):
+    """u_gamma = 0 (the first token with weight) and the largest float below 1
+    (the last one; the scan's rounding fallback): every sequence's final token
+    lies in the support of the distribution it is drawn from."""
+    import dataclasses
+    gam = [4, 4, 0, 2, 3, 1]
+    inp = _rand_custom(20007, gam, [0.8, 1.0, 0.9, 0.7, 1.1, 0.6], seed=21)
+    if tok:
+        inp = token_only(inp)
+    u = inp.uniforms.copy()
+    cu_t, g = inp.cu_t, inp.gammas
+    for b in range(inp.batch):
+        u[cu_t[b] + g[b]] = np.float32(ug)
+    inp = dataclasses.replace(inp, uniforms=u)
+    _, got = _check(inp, label=f"u_gamma={ug} token-only={tok}")
+    dt = inp.workload.dtype
+    for b in range(inp.batch):
+        n = int(got["accepted_len"][b])
+        assert 0 <= n <= g[b]
+        t = int(got["out_tokens"][cu_t[b] + n])
+        T = float(inp.temperatures[b])
+        lt = _as_f64(inp.target[cu_t[b] + n], dt) / T
+        p = np.exp(lt - lt.max())
+        p /= p.sum()
+        assert p[t] > 0.0, (b, n, t)
+        if n < g[b]:   # a rejected draft: the residual max(0, p - q) must not vanish at t
+            x = int(inp.draft_tokens[inp.cu_draft[b] + n])
+            if inp.draft is None:
+                q = np.zeros_like(p)
+                q[x] = 1.0
+            else:
+                ld = _as_f64(inp.draft[inp.cu_draft[b] + n], dt) / T
+                q = np.exp(ld - ld.max())
+                q /= q.sum()
+            if np.maximum(p - q, 0.0).sum() > 1e-6:
+                assert p[t] - q[t] > -1e-6 * max(p[t], q[t]), (b, n, t, p[t], q[t])
