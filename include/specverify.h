@@ -53,10 +53,12 @@
  * Problems in the data are detected on the device per sequence and
  * reported in accepted_len: -1 = invalid data (a NaN or +inf logit in any
  * of the sequence's rows, a row of only -inf, a drafted token outside
- * [0, V), a temperature that is negative, not finite or in (0, FLT_MIN)),
- * -2 = internal error: statistics of one of the sequence's rows were
- * missing when the sequence was resolved (not expected to happen; the
- * kernels always terminate).  The tokens of such a sequence are -1 and its
+ * [0, V), a temperature that is negative, not finite or in (0, FLT_MIN), a
+ * uniform of the sequence outside [0, 1) or NaN -- uniforms are draws from
+ * the unit interval, velog page, section 2 step 3), -2 = internal error:
+ * statistics of one of the sequence's rows were still missing after the
+ * bounded wait and its recomputation (not expected to happen; the kernels
+ * always terminate).  The tokens of such a sequence are -1 and its
  * diagnostics unspecified.
  */
 #ifndef SPECVERIFY_H_
@@ -110,7 +112,7 @@ typedef struct {
   const void* draft_logits;   /* [R_d, draft_stride]; NULL = token-only drafts      */
   int64_t draft_stride;
   const int32_t* draft_tokens;/* [R_d] drafted ids x_i; may be NULL iff R_d == 0   */
-  const float* uniforms;      /* [R_t] u in [0,1): uniforms[cu_t[b]+i], i < gamma_b,
+  const float* uniforms;      /* [R_t] u in [0,1) (else invalid data): uniforms[cu_t[b]+i], i < gamma_b,
                                  test draft i; uniforms[cu_t[b]+gamma_b] is the one
                                  uniform of the final (residual or bonus) sample   */
   const float* temperatures;  /* [B] T_b; 0 = greedy                               */
@@ -135,7 +137,8 @@ typedef struct {
 specverify_status specverify_create(const specverify_config* cfg, specverify_handle* out);
 
 /* Verify one batch, asynchronously on hip_stream (a hipStream_t; NULL = the
- * default stream).  Writes accepted_len, out_tokens and the non-NULL
+ * default stream): one kernel launch (two for a ragged batch, whose layout
+ * is checked first).  Writes accepted_len, out_tokens and the non-NULL
  * diagnostics; nothing else.  Errors (no launch happens): INVALID_ARGUMENT
  * for a NULL handle / inputs / outputs or required pointer, B > max_batch,
  * gamma outside [0, max_gamma], R_t > max_batch * (max_gamma + 1), a
@@ -186,8 +189,11 @@ specverify_status specverify_commit(specverify_handle h, const specverify_commit
 specverify_status specverify_destroy(specverify_handle h);
 
 /* Timing of a run's kernels, measured with HIP events recorded on the run's
- * stream: stream_ms covers the layout check (ragged batches only) and the
- * streaming pass over the logits, finish_ms the per-sequence finish.  set_timing(h, 1) starts a new
+ * stream: stream_ms covers every launch of the run (the layout check of a
+ * ragged batch, then the verification kernel, which streams the logits and
+ * resolves the sequences); finish_ms is the time between the end of those
+ * launches and the run's last event, about 0 (kept so that a caller can
+ * time work placed there).  set_timing(h, 1) starts a new
  * measurement: the next SPECVERIFY_TIMING_RUNS runs record their events (later
  * runs record none); set_timing(h, 0) stops recording.  timing_totals waits
  * for the last recorded run and returns the number of recorded runs and the

@@ -137,6 +137,109 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
+def _check_vec(name, t, dtype, device, n, required=True):
+    """A 1-D run of at least n elements of `dtype` on `device`, unit stride."""
+    if t is None:
+        if required and n > 0:
+            raise ValueError(f"{name} is required")
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the run needs {n}")
+
+
+def check_run_args(*, vocab, logits_dtype, device, target, draft, draft_tokens, uniforms, temperatures,
+                   accepted_len, out_tokens, gamma=None, cu_draft=None, num_draft_rows=None,
+                   diagnostics=()):
+    """Check the tensors of one run against the C ABI's layout before any of
+    their pointers is passed on (the library reads raw memory: a wrong dtype
+    would be misread, a short tensor read past its end).  Returns
+    (B, R_d, R_t).  Raises TypeError or ValueError.
+
+    ``device`` is the handle's torch device; ``diagnostics`` holds the
+    optional float32 outputs (p_draft, q_draft, beta, resid_mass), None
+    entries skipped."""
+    import torch
+    if temperatures is None or temperatures.dim() != 1:
+        raise ValueError("temperatures must be a 1-D tensor of B float32 values")
+    B = int(temperatures.shape[0])
+    if cu_draft is None:
+        if gamma is None or int(gamma) < 0:
+            raise ValueError("a uniform run needs gamma >= 0 (or cu_draft for a ragged one)")
+        R_d = B * int(gamma)
+    else:
+        if num_draft_rows is None:
+            raise ValueError("a ragged run needs num_draft_rows (the host copy of cu_draft[B])")
+        R_d = int(num_draft_rows)
+        if R_d < 0:
+            raise ValueError("num_draft_rows must be >= 0")
+        _check_vec("cu_draft", cu_draft, torch.int32, device, B + 1)
+    R_t = R_d + B
+    for name, t, rows in (("target", target, R_t), ("draft", draft, R_d)):
+        if t is None or (name == "draft" and t.numel() == 0):
+            if name == "target" and R_t > 0:
+                raise ValueError("target logits are required")
+            continue
+        if t.dtype != logits_dtype:
+            raise TypeError(f"{name} logits must be {logits_dtype}, got {t.dtype}")
+        if t.device != device:
+            raise ValueError(f"{name} logits must be on {device}, got {t.device}")
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} logits must be a 2-D tensor with unit column stride")
+        if t.shape[1] < vocab or t.stride(0) < vocab:
+            raise ValueError(f"{name} logits rows must hold the vocabulary ({vocab}), got shape "
+                             f"{tuple(t.shape)} stride {t.stride(0)}")
+        if t.shape[0] < rows:
+            raise ValueError(f"{name} logits have {t.shape[0]} rows, the run needs {rows}")
+    _check_vec("draft_tokens", draft_tokens, torch.int32, device, R_d)
+    _check_vec("uniforms", uniforms, torch.float32, device, R_t)
+    _check_vec("temperatures", temperatures, torch.float32, device, B)
+    _check_vec("accepted_len", accepted_len, torch.int32, device, B)
+    _check_vec("out_tokens", out_tokens, torch.int32, device, R_t)
+    for name, t in diagnostics:
+        _check_vec(name, t, torch.float32, device, R_d, required=False)
+    return B, R_d, R_t
+
+
+def check_commit_args(*, device, accepted_len, out_tokens, seq_tokens, seq_lens, gamma=None, cu_draft=None,
+                      num_draft_rows=None, appended=None, next_token=None):
+    """Check the tensors of one commit (see ``check_run_args``).  Returns
+    (B, R_t)."""
+    import torch
+    if accepted_len is None or accepted_len.dim() != 1:
+        raise ValueError("accepted_len must be a 1-D int32 tensor of B values")
+    B = int(accepted_len.shape[0])
+    if cu_draft is None:
+        if gamma is None or int(gamma) < 0:
+            raise ValueError("a uniform commit needs gamma >= 0 (or cu_draft)")
+        R_d = B * int(gamma)
+    else:
+        if num_draft_rows is None or int(num_draft_rows) < 0:
+            raise ValueError("a ragged commit needs num_draft_rows >= 0")
+        R_d = int(num_draft_rows)
+        _check_vec("cu_draft", cu_draft, torch.int32, device, B + 1)
+    R_t = R_d + B
+    _check_vec("accepted_len", accepted_len, torch.int32, device, B)
+    _check_vec("out_tokens", out_tokens, torch.int32, device, R_t)
+    _check_vec("seq_lens", seq_lens, torch.int32, device, B)
+    _check_vec("appended", appended, torch.int32, device, B, required=False)
+    _check_vec("next_token", next_token, torch.int32, device, B, required=False)
+    if seq_tokens is None or seq_tokens.dim() != 2 or seq_tokens.stride(1) != 1:
+        raise ValueError("seq_tokens must be a 2-D tensor with unit column stride")
+    if seq_tokens.dtype != torch.int32:
+        raise TypeError(f"seq_tokens must be torch.int32, got {seq_tokens.dtype}")
+    if seq_tokens.device != device:
+        raise ValueError(f"seq_tokens must be on {device}, got {seq_tokens.device}")
+    if seq_tokens.shape[0] < B:
+        raise ValueError(f"seq_tokens has {seq_tokens.shape[0]} rows, the commit needs {B}")
+    return B, R_t
+
+
 class SpecVerify:
     """A handle bound to one device, vocabulary and logits dtype.
 
@@ -187,25 +290,22 @@ class SpecVerify:
             p_draft=None, q_draft=None, beta=None, resid_mass=None, stream=None) -> None:
         import torch
         want = torch.float32 if self.dtype == F32 else torch.bfloat16
-        for name, t in (("target", target), ("draft", draft)):
-            if t is None or t.numel() == 0:
-                continue
-            if t.dtype != want:
-                raise TypeError(f"{name} logits must be {want}, got {t.dtype}")
-            if t.dim() != 2 or t.stride(1) != 1:
-                raise ValueError(f"{name} logits must be a 2-D tensor with unit column stride")
-        batch = int(temperatures.shape[0])
+        batch, R_d, _ = check_run_args(
+            vocab=self.vocab, logits_dtype=want, device=torch.device("cuda", self.device), target=target,
+            draft=draft, draft_tokens=draft_tokens, uniforms=uniforms, temperatures=temperatures,
+            accepted_len=accepted_len, out_tokens=out_tokens, gamma=gamma, cu_draft=cu_draft,
+            num_draft_rows=num_draft_rows,
+            diagnostics=(("p_draft", p_draft), ("q_draft", q_draft), ("beta", beta), ("resid_mass", resid_mass)))
         inp = Inputs()
         inp.batch = batch
         if cu_draft is None:
             inp.gamma = int(gamma)
             inp.cu_draft = None
-            inp.num_draft_rows = batch * int(gamma)
+            inp.num_draft_rows = R_d
         else:
             inp.gamma = 0
             inp.cu_draft = _ptr(cu_draft)
-            inp.num_draft_rows = int(num_draft_rows if num_draft_rows is not None
-                                     else (draft_tokens.shape[0] if draft_tokens is not None else 0))
+            inp.num_draft_rows = R_d
         inp.target_logits = _ptr(target)
         inp.target_stride = int(target.stride(0))
         # draft None with drafted tokens: token-only drafts (q_i = delta_{x_i})
@@ -228,18 +328,20 @@ class SpecVerify:
         ``seq_tokens`` [B, capacity] (int32, device) at ``seq_lens`` [B]; see
         specverify_commit in include/specverify.h."""
         import torch
-        if seq_tokens.dim() != 2 or seq_tokens.stride(1) != 1:
-            raise ValueError("seq_tokens must be a 2-D tensor with unit column stride")
+        B, R_t = check_commit_args(device=torch.device("cuda", self.device), accepted_len=accepted_len,
+                                   out_tokens=out_tokens, seq_tokens=seq_tokens, seq_lens=seq_lens, gamma=gamma,
+                                   cu_draft=cu_draft, num_draft_rows=num_draft_rows, appended=appended,
+                                   next_token=next_token)
         a = CommitArgs()
-        a.batch = int(accepted_len.shape[0])
+        a.batch = B
         if cu_draft is None:
             a.gamma = int(gamma)
             a.cu_draft = None
-            a.num_draft_rows = a.batch * int(gamma)
+            a.num_draft_rows = R_t - B
         else:
             a.gamma = 0
             a.cu_draft = _ptr(cu_draft)
-            a.num_draft_rows = int(num_draft_rows)
+            a.num_draft_rows = R_t - B
         a.accepted_len = _ptr(accepted_len)
         a.out_tokens = _ptr(out_tokens)
         a.seq_tokens = _ptr(seq_tokens)

@@ -7,22 +7,22 @@
 // Scale Your Model -- All About Transformer Inference", Appendix D): see
 // include/specverify.h.
 //
-// A run launches up to three kernels on the caller's stream.
+// A run is one launch of verify_kernel on the caller's stream (two for a
+// ragged batch: layout_kernel first checks cu_draft and writes one record
+// per target row plus the split of the batch into row groups).
 //
-// layout_kernel (ragged batches only) checks cu_draft and writes one
-// record per target row: sequence, draft row, whether the position has a
-// draft, temperature.
+// Work is split into eight row groups, one per XCD of an MI355X
+// (workgroup b runs on XCD b % 8).  A group owns a contiguous range of
+// whole sequences, so every row of a sequence, and every value its waves
+// exchange, stays in one XCD's L2.  The grid is persistent: what the GPU
+// holds at once.
 //
-// stream_kernel reads every logit from HBM exactly once.  Its unit of work
-// is an item: 4 KB of one target row (a chunk of 2048 bf16 or 1024 fp32
-// logits) plus the same chunk of the draft row when the position has one,
-// so p_k and q_k of a token meet in the same lane.  One wave owns one item
-// at a time; the four waves of a workgroup are independent (no barriers,
-// no LDS).  The grid is persistent (what the GPU holds at once).  Rows are
-// dealt round robin to eight groups matching the eight XCDs (workgroup b
-// runs on XCD b % 8); wave j of a group takes items j, j + Gw, j + 2 Gw, ...
-// of the group's row-major item list, so the chunks of a row are handled in
-// one round by waves of one XCD.
+// Streaming.  The unit of work is an item: 4 KB of one target row (a chunk
+// of 2048 bf16 or 1024 fp32 logits) plus the same chunk of the draft row
+// when the position has one, so p_k and q_k of a token meet in the same
+// lane.  One wave owns one item at a time; wave j of a group takes items
+// j, j + Gw, j + 2 Gw, ... of the group's row-major item list, so the chunks
+// of a row are handled in one round by different waves.
 //   phase 1   chunk max m_c (DPP), e_k = 2^(l_k s - m_c s) with s = log2(e)/T
 //             kept in registers, chunk sum s_c; (m_c, s_c) of target and
 //             draft go out in epoch-tagged slots.  T = 0: chunk argmax.
@@ -31,41 +31,40 @@
 //             rho = a_d / a_t, p_k = a_t e_t and q_k = a_t rho e_d, so
 //             min(p, q) = a_t min(e_t, rho e_d) and max(0, p - q) =
 //             a_t (e_t - min(e_t, rho e_d)); the chunk sums of both (beta,
-//             velog section 2-3 item 1; residual mass Z, item 2) go out.
+//             velog section 2-3 item 1; residual mass Z, item 2) go out in
+//             epoch-tagged partials.
 // The waves are software pipelined: a step runs phase 1 of item k + 1, then
 // polls item k's row and runs its phase 2, with the 16-byte loads of items
-// k + 2 and k + 3 in flight.  Logits are read with buffer loads: a row
-// without a draft gets a zero-sized buffer, so every item issues the same
-// loads and none of them touches memory it should not.
-//
-// stream_t_kernel replaces stream_kernel when a run has no draft logits
-// (token-only drafts, q = delta_x; or no drafts at all): phase 1 only, one
-// item per wave, no exchange.  The chunk that holds a drafted token x also
+// k + 2 and k + 3 in flight.  Logits are read with buffer loads over one
+// chunk: a row without a draft gets a zero-sized buffer, so every item
+// issues the same loads and none of them touches memory it should not.
+// Without draft logits (token-only drafts, q = delta_x; or no drafts at
+// all) only phase 1 runs, and the chunk that holds a drafted token x also
 // publishes e_t at x.
 //
-// finish_kernel, one workgroup per sequence and one wave per row, then
-// merges the partials: Z and beta; the chunk whose CDF interval holds
-// u_gamma * Z (or the CDF of p for the bonus row and when Z = 0), whose
-// logits it re-reads; p(x) and q(x) from the two logits of the drafted token
-// (a token-only draft: e_t at x from the slots, q(x) = 1); the acceptance
-// test u_i q(x) < p(x); for a rejected row, the scan of the re-read chunk
-// in token order for the token; finally the sequence's first rejection n,
-// accepted_len and the n + 1 tokens.  The accepted length never leaves the
-// device.
+// Resolution.  When a workgroup has streamed its items, it resolves the
+// sequences dealt to it, one at a time: its waves take the sequence's rows
+// and merge that row's slots and partials (Z and beta); find the chunk
+// whose CDF interval holds u_gamma * Z (or the CDF of p for the bonus row
+// and when Z = 0) and re-read it; form p(x) and q(x) from the two logits of
+// the drafted token (a token-only draft: e_t at x from the slots, q(x) = 1);
+// test u_i q(x) < p(x); and, for a rejected row, scan the re-read chunk in
+// token order for the token.  The row results meet in LDS, where one wave
+// finds the sequence's first rejection n and writes accepted_len and the
+// n + 1 tokens.  The accepted length never leaves the device.
 //
 // commit_kernel (its own call, specverify_commit) appends each sequence's
 // n + 1 emitted tokens to its token row on the device.
 //
-// Inside stream_kernel, values cross waves only in 64-bit slots that carry a
-// 32-bit epoch tag next to the value.  A slot is written with one aligned
-// 64-bit store (the CU's L1 writes through to the XCD's L2) and polled with
-// loads that skip L1 and read that L2; the waves that meet over a row all run
-// on one XCD, so a reader that sees the tag sees the value, without fences or
+// Values cross waves only in 64-bit slots and 16-byte partials that carry a
+// 32-bit epoch tag next to the value.  They are written with plain stores
+// (the CU's L1 writes through to the XCD's L2) and polled with loads that
+// skip L1 and read that L2; the waves that meet over a row all run on one
+// XCD, so a reader that sees the tag sees the value, without fences or
 // atomics.  Nothing guarantees that every workgroup of the grid is resident
 // at once, so a wave that has polled spin_limit times reads the chunks that
-// are still missing and computes their statistics itself (bit-identical to
-// what their owners publish); every wait therefore ends.  finish_kernel reads
-// what stream_kernel wrote after the kernel boundary.
+// are still missing and computes their slots and partials itself
+// (bit-identical to what their owners publish); every wait therefore ends.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -76,7 +75,7 @@
 
 namespace {
 
-constexpr int kStreamWaves = 4;                // independent waves per stream workgroup
+constexpr int kStreamWaves = 4;                // waves per workgroup
 constexpr int kStreamThreads = 64 * kStreamWaves;
 constexpr int kU = 4;                          // 16-byte loads per lane and row of an item
 constexpr int kRowBytes = kU * 64 * 16;        // bytes of one row in one item (4 KB)
@@ -86,7 +85,6 @@ constexpr int kGroups = 8;                     // row groups = XCDs of an MI355X
 constexpr int kX1 = 4;                         // exchange slots per (row, chunk)
 constexpr int kPart = 4;                       // floats of partials per (row, chunk)
 constexpr int kMaxGamma = 255;                 // rows per sequence <= 256
-constexpr int kFinishWaves = 8;
 constexpr int kLayoutThreads = 1024;
 constexpr int kDefaultSpin = 64;               // polls (~1 us each) before a wave computes missing chunks itself
 constexpr int kMaxSpin = 1 << 20;
@@ -98,6 +96,7 @@ constexpr uint32_t kAccBit = 1u << 23;
 constexpr uint32_t kStatusShift = 24;          // 0 ok, 1 invalid data, 2 wait expired
 constexpr int kRsrcWord3 = 0x00020000;         // raw (untyped) buffer, gfx9 family
 constexpr int kNT = 2;                         // buffer-load cache policy: nontemporal
+constexpr int kSC1 = 16;                       // buffer-load cache policy sc1: the load misses L1 and reads L2
 
 // Partials of one (row, chunk), kPart floats: the epoch that completed the
 // item (bits), the sum of e_t - min(e_t, rho e_d), the sum of
@@ -122,22 +121,26 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 struct Params {
   const char* target;
-  const char* draft;
-  int64_t tstride_b;         // row strides in bytes
-  int64_t dstride_b;
+  const char* draft;         // NULL: no draft logits in this launch
+  uint32_t tstride_b;        // row strides in bytes (< 2^31)
+  uint32_t dstride_b;
   const int32_t* tokens;
   const float* uniforms;
   const float* temps;
   const int32_t* cu_draft;   // NULL: uniform gamma
-  const int4* rowinfo;       // ragged: per target row {sequence (<0: bad layout), draft row, has draft, T bits}
+  const int4* rowinfo;       // ragged: per target row {sequence, draft row, has draft, T bits}
   const uint32_t* layout;    // ragged: epoch * 2 + (layout invalid)
+  const int32_t* gbounds;    // ragged: [2 (kGroups + 1)] row bounds, then sequence bounds, of the groups
+  int32_t grow[kGroups + 1]; // uniform gamma: first target row of each group (and R_t)
+  int32_t gseq[kGroups + 1]; // uniform gamma: first sequence of each group (and B)
   int32_t gamma;
   int32_t B;
   int32_t R_d;
   int32_t R_t;
   int32_t V;
   int32_t C;                 // chunks per row
-  int32_t Gw;                // stream waves per row group
+  int32_t Gw;                // waves per row group
+  int32_t Wg;                // workgroups per row group
   int32_t max_gamma;
   uint32_t epoch;
   int32_t spin_limit;
@@ -145,7 +148,7 @@ struct Params {
   uint32_t div_c[3];         // unsigned division by C: multiplier and two shifts
   uint32_t div_g[3];         // unsigned division by gamma + 1 (uniform gamma)
   uint64_t* xch1;            // [rows][C][kX1] tagged slots
-  uint64_t* dummy;           // [stream waves][8]: where a wave's step with nothing to publish writes
+  uint64_t* dummy;           // [waves][8]: where a wave's step with nothing to publish writes
   float* part;               // [rows][C][kPart]
   int32_t* acc_len;
   int32_t* out_tokens;
@@ -158,7 +161,7 @@ struct Params {
 // ------------------------------------------------------------------ slots
 
 // One 64-bit store (single-copy atomic); the CU's L1 writes it through to
-// the XCD's L2, where the sc0 loads of the other waves of the row find it.
+// the XCD's L2, where the sc1 loads of the other waves of the row find it.
 __device__ __forceinline__ void slot_put(uint64_t* p, uint32_t tag, uint32_t v) {
   *p = ((uint64_t)tag << 32) | v;
 }
@@ -278,21 +281,36 @@ __device__ __forceinline__ void wave_argmax(float& v, int& k) {
   k = bk;
 }
 
-// Exponent offset of a chunk: -m s, or 0 for a chunk of only -inf (so that
-// its exponentials are 2^-inf = 0 instead of NaN).
+// Exponent offset of a chunk: -m s rounded, or 0 for a chunk of only -inf
+// (so that its exponentials are 2^-inf = 0 instead of NaN).  A chunk's
+// exponentials are e_k = 2^(l_k s + offset).
 __device__ __forceinline__ float chunk_offset(float m, float s) {
   return (m == -__builtin_huge_valf()) ? 0.0f : -m * s;
 }
+// The offset's rounding error: -m s = chunk_offset(m, s) + chunk_lo(m, s)
+// exactly (the error of a rounded product is a float, and one fma gives it
+// exactly).  The e_k of the chunk carry the factor 2^-lo; the chunk's scale
+// puts it back, so the offset's rounding (up to 2^-25 |m s|, a few 1e-5 at
+// low temperatures) never reaches p, q, beta or Z.
+__device__ __forceinline__ float chunk_lo(float m, float s) {
+  return (m == -__builtin_huge_valf()) ? 0.0f : __builtin_fmaf(-m, s, -chunk_offset(m, s));
+}
+// Exponent of a chunk's scale against the row maximum M: (m - M) s + lo,
+// so that p_k = 2^(chunk_exp) e_k / S.
+__device__ __forceinline__ float chunk_exp(float m, float M, float s) {
+  return __builtin_fmaf(m - M, s, chunk_lo(m, s));
+}
 // Scale of a chunk: p_k = scale * e_k.
 __device__ __forceinline__ float chunk_scale(float m, float M, float S, float s) {
-  return __builtin_amdgcn_exp2f((m - M) * s) / S;
+  return __builtin_amdgcn_exp2f(chunk_exp(m, M, s)) / S;
 }
 // rho = a_d / a_t of a chunk (q_k = a_t rho e_d), from the chunk maxima and
-// the row normalisers: 2^(((m_d - M_d) - (m_t - M_t)) s) S_t / S_d.  Both
-// kernels take it from this function, so a chunk's residual weights
-// e_t - min(e_t, rho e_d) have the same bits in both.
+// the row normalisers: 2^(((m_d - M_d) - (m_t - M_t)) s + lo_d - lo_t) S_t / S_d.
+// Every wave takes it from this function, so a chunk's residual weights
+// e_t - min(e_t, rho e_d) have the same bits wherever they are computed.
 __device__ __forceinline__ float chunk_rho(float mt, float Mt, float St, float md, float Md, float Sd, float s) {
-  return __builtin_amdgcn_exp2f(((md - Md) - (mt - Mt)) * s) * (St * __builtin_amdgcn_rcpf(Sd));
+  return __builtin_amdgcn_exp2f(__builtin_fmaf((md - Md) - (mt - Mt), s, chunk_lo(md, s) - chunk_lo(mt, s))) *
+         (St * __builtin_amdgcn_rcpf(Sd));
 }
 // min(a, b) of two floats that are >= 0 (+0, positive, +inf or a positive
 // NaN): the unsigned order of their bit patterns is their order, NaN above
@@ -307,28 +325,29 @@ __device__ __forceinline__ float resid_w(float et, float ed, float rho) {
   return et - min_nonneg(et, rho * ed);
 }
 
-// ------------------------------------------------------------------ chunk slots of a row
+
+// ------------------------------------------------------------------ chunk slots and partials of a row
 
 // The exchange slots of every chunk of row r, lane-major: lane l holds
-// chunks l, l + 64, ...  Lanes past the last chunk read the dummy slots.
+// chunks l, l + 64, ...  Lanes past the last chunk re-read the last one,
+// whose values they never use.
 template <int NPER>
 struct RowSlots {
   uint64_t w[NPER][kX1];
 };
-// Byte offsets of a lane's slots inside a row (loop invariant; lanes past
-// the last chunk re-read the last one, whose values they never use).
+// Byte offsets of a lane's chunk records inside a row, `bytes` per chunk
+// (loop invariant).
 template <int NPER>
-__device__ __forceinline__ void slot_offsets(int C, int lane, uint32_t (&off)[NPER]) {
+__device__ __forceinline__ void chunk_offsets(int C, int lane, int bytes, uint32_t (&off)[NPER]) {
 #pragma unroll
-  for (int j = 0; j < NPER; ++j) off[j] = (uint32_t)min(lane + 64 * j, C - 1) * (kX1 * sizeof(uint64_t));
+  for (int j = 0; j < NPER; ++j) off[j] = (uint32_t)min(lane + 64 * j, C - 1) * (uint32_t)bytes;
 }
 // The slots of row r, read two at a time with 16-byte buffer loads that miss
-// the CU's L1 (sc1) and are served by the XCD's L2 (0.5 us per launch faster
-// than one 8-byte load per slot), through a buffer over the row's slots:
-// a uniform base and loop-invariant lane offsets, so no vector register is
-// written before the loads issue.  `real` false: a zero-sized buffer, the
-// loads read zeros (tag 0 is never an epoch) and touch no memory.
-constexpr int kSC0 = 16;   // sc1: the load misses L1 and reads L2
+// the CU's L1 (sc1) and are served by the XCD's L2, through a buffer over
+// the row's slots: a uniform base and loop-invariant lane offsets, so no
+// vector register is written before the loads issue.  `real` false: a
+// zero-sized buffer, the loads read zeros (tag 0 is never an epoch) and
+// touch no memory.
 template <int NPER>
 __device__ __forceinline__ void slots_issue(const Params& P, int r, bool real, const uint32_t (&off)[NPER],
                                             RowSlots<NPER>& q) {
@@ -339,27 +358,47 @@ __device__ __forceinline__ void slots_issue(const Params& P, int r, bool real, c
   for (int j = 0; j < NPER; ++j)
 #pragma unroll
     for (int k = 0; k < kX1; k += 2) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off[j] + k * 8, 0, kSC0);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off[j] + k * 8, 0, kSC1);
       q.w[j][k] = (uint64_t)v[0] | ((uint64_t)v[1] << 32);
       q.w[j][k + 1] = (uint64_t)v[2] | ((uint64_t)v[3] << 32);
     }
 }
-// Every chunk's first `n` slots carry `tag` (wave-uniform answer).
+// Every chunk's slots carry `tag` (wave-uniform answer).
 template <int NPER>
-__device__ __forceinline__ bool slots_ready(const RowSlots<NPER>& q, int C, uint32_t tag, int n, int lane) {
+__device__ __forceinline__ bool slots_ready(const RowSlots<NPER>& q, int C, uint32_t tag, int lane) {
   bool ok = true;
 #pragma unroll
   for (int j = 0; j < NPER; ++j)
     if (lane + 64 * j < C) {
 #pragma unroll
-      for (int k = 0; k < kX1; ++k)
-        if (k < n) ok &= slot_tag(q.w[j][k]) == tag;
+      for (int k = 0; k < kX1; ++k) ok &= slot_tag(q.w[j][k]) == tag;
     }
   return __all(ok);
 }
+// The partials of row r (one 16-byte load per chunk, sc1 as the slots).
+template <int NPER>
+__device__ __forceinline__ void part_issue(const Params& P, int r, bool real, const uint32_t (&off)[NPER],
+                                           float4 (&pt)[NPER]) {
+  const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc((void*)(P.part + (int64_t)(real ? r : 0) * P.C * kPart),
+                                                    (short)0, real ? P.C * kPart * (int)sizeof(float) : 0,
+                                                    kRsrcWord3);
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off[j], 0, kSC1);
+    pt[j] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+  }
+}
+template <int NPER>
+__device__ __forceinline__ bool parts_ready(const float4 (&pt)[NPER], int C, uint32_t tag, int lane) {
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j)
+    if (lane + 64 * j < C) ok &= __float_as_uint(pt[j].x) == tag;
+  return __all(ok);
+}
 // Row normalisers of a softmax split into chunks from slots (m_c, s_c) at
-// slot index `at`: M = max m_c, S = sum s_c 2^((m_c - M) s).  Both kernels
-// call this with the same lane layout.
+// slot index `at`: M = max m_c, S = sum s_c 2^((m_c - M) s).  Every caller
+// uses the same lane layout, so every wave gets the same bits.
 template <int NPER>
 __device__ __forceinline__ void merge_row(const RowSlots<NPER>& q, int C, int at, float s, int lane, float& M,
                                           float& S) {
@@ -371,7 +410,7 @@ __device__ __forceinline__ void merge_row(const RowSlots<NPER>& q, int C, int at
   float a = 0.0f;
 #pragma unroll
   for (int j = 0; j < NPER; ++j)
-    if (lane + 64 * j < C) a += slot_f(q.w[j][at + 1]) * __builtin_amdgcn_exp2f((slot_f(q.w[j][at]) - M) * s);
+    if (lane + 64 * j < C) a += slot_f(q.w[j][at + 1]) * __builtin_amdgcn_exp2f(chunk_exp(slot_f(q.w[j][at]), M, s));
   S = wave_sum(a);
 }
 __device__ __forceinline__ bool norm_ok(float M, float S) {
@@ -380,23 +419,29 @@ __device__ __forceinline__ bool norm_ok(float M, float S) {
 
 // ------------------------------------------------------------------ loads
 
-__device__ __forceinline__ Rsrc row_rsrc(const char* base, int64_t row, int64_t stride_b, int nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row * stride_b), (short)0, nbytes, kRsrcWord3);
+// A raw buffer over chunk c of a row: bytes c * kRowBytes .. nb of the row.
+// Every load through it uses a vector offset relative to the chunk start,
+// which the hardware checks against the buffer's size, so bytes past the
+// row end read as 0 and no load leaves the row.  live false: a zero-sized
+// buffer (every load reads 0 and touches no memory).
+__device__ __forceinline__ Rsrc chunk_rsrc(const char* base, int row, uint32_t stride_b, int c, int nb,
+                                           bool live) {
+  // the address is formed whatever `live` is: a zero-sized buffer never touches memory
+  const char* p = base + (uint64_t)(uint32_t)row * stride_b + (uint32_t)(c * kRowBytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, live ? nb - c * kRowBytes : 0, kRsrcWord3);
 }
 
-// Loads of one row of chunk c: vector u of lane `lane` holds tokens
-// c*CH + u*64*EPV + lane*EPV .. +EPV-1.  VEC: 16-byte loads (rows and V*esize
-// on 16-byte boundaries); otherwise element loads.  Bytes past the buffer
-// read as 0 (the caller turns tokens >= V into -inf).
+// Load u of one row of a chunk: lane `lane` gets tokens u*64*EPV +
+// lane*EPV .. +EPV-1 of the chunk.  VEC: one 16-byte load (rows and V*esize
+// on 16-byte boundaries); otherwise element loads.
 template <int DT, bool VEC>
-__device__ __forceinline__ u32x4 load_vec(Rsrc rs, int c, int u, int lane) {
+__device__ __forceinline__ u32x4 load_vec(Rsrc rs, int u, int lane) {
   using F = Fmt<DT>;
   u32x4 w;
   if (VEC) {
-    // the lane's offset is loop invariant; the chunk's goes into the scalar offset
-    w = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + u * 1024, c * kRowBytes, kNT);
+    w = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + u * 1024, 0, kNT);
   } else {
-    const int t0 = c * F::CH + u * 64 * F::EPV + lane * F::EPV;
+    const int t0 = u * 64 * F::EPV + lane * F::EPV;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (DT == SPECVERIFY_F32) {
@@ -411,9 +456,9 @@ __device__ __forceinline__ u32x4 load_vec(Rsrc rs, int c, int u, int lane) {
   return w;
 }
 template <int DT, bool VEC>
-__device__ __forceinline__ void issue_row(Rsrc rs, int c, int lane, u32x4 (&raw)[kU]) {
+__device__ __forceinline__ void issue_row(Rsrc rs, int lane, u32x4 (&raw)[kU]) {
 #pragma unroll
-  for (int u = 0; u < kU; ++u) raw[u] = load_vec<DT, VEC>(rs, c, u, lane);
+  for (int u = 0; u < kU; ++u) raw[u] = load_vec<DT, VEC>(rs, u, lane);
 }
 
 template <int DT>
@@ -451,33 +496,25 @@ __device__ __forceinline__ void mask_tail2(float (&x)[Fmt<DT>::L], float (&y)[Fm
       __builtin_amdgcn_sched_barrier(0);
     }
 }
-// Token of element (u, e) of a lane.
+// Token of element k = u * EPV + e of a lane in chunk c.
 template <int DT>
 __device__ __forceinline__ int token_of(int c, int k, int lane) {
   using F = Fmt<DT>;
   const int u = k / F::EPV, e = k - u * F::EPV;
   return c * F::CH + u * 64 * F::EPV + lane * F::EPV + e;
 }
-// Element e of vector u of a lane, as unpack and mask_tail2 leave it; `lim`
-// is V minus the token of element 0 of the vector (tokens >= V are -inf).
-template <int DT>
-__device__ __forceinline__ float elem(const u32x4& w, int e, int lim) {
-  float x;
-  if (DT == SPECVERIFY_F32) {
-    x = __uint_as_float(w[e]);
-  } else {
-    const uint32_t h = w[e >> 1];
-    x = __uint_as_float((e & 1) ? (h & 0xFFFF0000u) : (h << 16));
-  }
-  return e >= lim ? -__builtin_huge_valf() : x;
-}
-
 // Element e of a lane's 16-byte vector w, as unpack leaves it.
 template <int DT>
 __device__ __forceinline__ float vec_elem(const u32x4& w, int e) {
   if (DT == SPECVERIFY_F32) return __uint_as_float(w[e]);
   const uint32_t h = w[e >> 1];
   return __uint_as_float((e & 1) ? (h & 0xFFFF0000u) : (h << 16));
+}
+// The same, with tokens >= V as -inf; `lim` is V minus the token of element
+// 0 of the vector.
+template <int DT>
+__device__ __forceinline__ float elem(const u32x4& w, int e, int lim) {
+  return e >= lim ? -__builtin_huge_valf() : vec_elem<DT>(w, e);
 }
 // Tokens >= V of the last chunk become -inf in the raw words of a row (one
 // comparison per token, as in mask_tail2).
@@ -523,7 +560,7 @@ __device__ __forceinline__ uint32_t udiv(uint32_t n, const uint32_t (&k)[3]) {
 }
 
 struct RowMeta {
-  int b;      // sequence (< 0: the batch layout is invalid)
+  int b;      // sequence
   int rd;     // draft row
   int pair;   // position has a draft
   float T;
@@ -547,13 +584,38 @@ __device__ __forceinline__ RowMeta row_meta(const Params& P, int r) {
   return m;
 }
 __device__ __forceinline__ bool t_sampled(float T) { return T >= kFltMin && T <= kFltMax; }
+__device__ __forceinline__ bool u_ok(float u) { return u >= 0.0f && u < 1.0f; }   // false for NaN
+
+// Rows [r0, r1) and sequences [s0, s1) of row group g.
+struct Group {
+  int r0, r1, s0, s1;
+};
+__device__ __forceinline__ Group group_of(const Params& P, int g) {
+  Group G;
+  if (P.gbounds == nullptr) {
+    G.r0 = P.grow[g];
+    G.r1 = P.grow[g + 1];
+    G.s0 = P.gseq[g];
+    G.s1 = P.gseq[g + 1];
+  } else {
+    G.r0 = ld_const(P.gbounds, g);
+    G.r1 = ld_const(P.gbounds, g + 1);
+    G.s0 = ld_const(P.gbounds, kGroups + 1 + g);
+    G.s1 = ld_const(P.gbounds, kGroups + 2 + g);
+  }
+  return G;
+}
 
 // ================================================================== layout kernel (ragged batches)
 
 // One workgroup: checks that cu_draft is a layout (cu_draft[0] = 0,
-// cu_draft[B] = R_d, 0 <= gamma_b <= max_gamma) and writes every target row's
-// record; an invalid layout marks every row.
-__global__ __launch_bounds__(kLayoutThreads) void layout_kernel(Params P, int4* rowinfo, uint32_t* flag) {
+// cu_draft[B] = R_d, 0 <= gamma_b <= max_gamma); writes every target row's
+// record and splits the batch into kGroups ranges of whole sequences with
+// about R_t / kGroups target rows each (group g starts at the first
+// sequence b whose first target row cu_draft[b] + b is at least
+// g R_t / kGroups).  An invalid layout makes every group empty.
+__global__ __launch_bounds__(kLayoutThreads) void layout_kernel(Params P, int4* rowinfo, int32_t* gbounds,
+                                                                uint32_t* flag) {
   const int tid = threadIdx.x;
   int bad = 0;
   for (int b = tid; b < P.B; b += blockDim.x) {
@@ -563,22 +625,35 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(Params P, int4* 
   if (tid == 0) bad |= P.cu_draft[0] != 0 || P.cu_draft[P.B] != P.R_d;
   bad = __syncthreads_or(bad);
   if (bad) {
-    for (int r = tid; r < P.R_t; r += blockDim.x) rowinfo[r] = make_int4(-1, 0, 0, 0);
+    if (tid < 2 * (kGroups + 1)) gbounds[tid] = 0;
   } else {
     for (int b = tid; b < P.B; b += blockDim.x) {
       const int d0 = P.cu_draft[b], g = P.cu_draft[b + 1] - d0;
       const int Tb = __float_as_int(P.temps[b]);
       for (int i = 0; i <= g; ++i) rowinfo[d0 + b + i] = make_int4(b, d0 + i, i < g ? 1 : 0, Tb);
     }
+    if (tid <= kGroups) {
+      // first sequence whose first target row reaches tid * R_t / kGroups
+      const int64_t want = ((int64_t)tid * P.R_t + kGroups - 1) / kGroups;
+      int lo = 0, hi = P.B;   // answer in [lo, hi]
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)P.cu_draft[mid] + mid >= want) hi = mid;
+        else lo = mid + 1;
+      }
+      gbounds[tid] = P.cu_draft[lo] + lo;            // first target row of the group
+      gbounds[kGroups + 1 + tid] = lo;               // first sequence of the group
+    }
   }
   if (tid == 0) *flag = P.epoch * 2u + (bad ? 1u : 0u);
 }
 
-// ================================================================== stream kernel
+// ================================================================== streaming pass
 
 // An item in three scalar registers: target row (bits 0-23) and chunk (bits
 // 24-31); draft row (bits 0-23), mode (bits 24-25: 0 nothing to do,
-// 1 sampled, 2 greedy) and whether the position has a draft (bit 26);
+// 1 sampled, 2 greedy), whether the launch reads the position's draft
+// logits (bit 26) and whether the position has a drafted token (bit 27);
 // log2(e) / T.  Rows < 2^24 and chunks <= 256 fit.
 struct Item {
   uint32_t rc, rdf;
@@ -587,10 +662,12 @@ struct Item {
   __device__ __forceinline__ int c() const { return (int)(rc >> 24); }
   __device__ __forceinline__ int rd() const { return (int)(rdf & 0xFFFFFFu); }
   __device__ __forceinline__ int mode() const { return (int)((rdf >> 24) & 3u); }
-  __device__ __forceinline__ bool pair() const { return (rdf >> 26) & 1u; }
+  __device__ __forceinline__ bool pair() const { return (rdf >> 26) & 1u; }   // draft logits read
+  __device__ __forceinline__ bool drafted() const { return (rdf >> 27) & 1u; }
 };
 
-__device__ __forceinline__ Item make_item(const Params& P, int grp, int idx, int n_items) {
+// Item `idx` of the row-major item list of a group whose rows start at r0.
+__device__ __forceinline__ Item make_item(const Params& P, int r0, int idx, int n_items) {
   Item it;
   it.rc = 0;
   it.rdf = 0;
@@ -598,10 +675,9 @@ __device__ __forceinline__ Item make_item(const Params& P, int grp, int idx, int
   if (idx >= n_items) return it;
   const int rl = (int)udiv((uint32_t)idx, P.div_c);
   const int c = idx - rl * P.C;
-  const int r = grp + kGroups * rl;
+  const int r = r0 + rl;
   it.rc = (uint32_t)r | ((uint32_t)c << 24);
   const RowMeta m = row_meta(P, r);
-  if (m.b < 0) return it;   // invalid layout: nothing is read
   uint32_t mode = 0;
   if (t_sampled(m.T)) {
     mode = 1;
@@ -610,27 +686,29 @@ __device__ __forceinline__ Item make_item(const Params& P, int grp, int idx, int
     mode = 2;
   }   // any other temperature is invalid data: nothing is read
   // a token-only draft has no logits: its position streams like one without a draft
-  it.rdf = (uint32_t)m.rd | (mode << 24) | ((uint32_t)(m.pair != 0 && !P.token_only) << 26);
+  it.rdf = (uint32_t)m.rd | (mode << 24) | ((uint32_t)(m.pair != 0 && !P.token_only) << 26) |
+           ((uint32_t)(m.pair != 0) << 27);
   return it;
 }
 
 // The item's loads: always the same 2 kU (VEC) instructions; absent rows
-// read through zero-sized buffers.  issue_target: the target row alone, for
-// launches without draft logits.
-template <int DT, bool VEC>
+// read through zero-sized buffers.  Element loads (rows not on 16-byte
+// boundaries, a rare layout) are not prefetched: phase 1 issues them itself
+// (NOW), which keeps the many element loads of a prefetch out of the
+// registers of the pipeline.
+template <int DT, bool VEC, bool NOW = false>
 __device__ __forceinline__ void issue_item(const Params& P, const Item& it, int lane, u32x4 (&R)[2][kU]) {
+  if (!VEC && !NOW) return;
   const int nb = P.V * Fmt<DT>::ESIZE;
   const bool live = it.mode() != 0;
-  const Rsrc rt = row_rsrc(P.target, live ? it.r() : 0, P.tstride_b, live ? nb : 0);
-  const Rsrc rd = row_rsrc(P.draft, (live && it.pair()) ? it.rd() : 0, P.dstride_b, (live && it.pair()) ? nb : 0);
-  issue_row<DT, VEC>(rt, it.c(), lane, R[0]);
-  issue_row<DT, VEC>(rd, it.c(), lane, R[1]);
+  issue_row<DT, VEC>(chunk_rsrc(P.target, it.r(), P.tstride_b, it.c(), nb, live), lane, R[0]);
+  issue_row<DT, VEC>(chunk_rsrc(P.draft, it.rd(), P.dstride_b, it.c(), nb, live && it.pair()), lane, R[1]);
 }
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool NOW = false>
 __device__ __forceinline__ void issue_target(const Params& P, const Item& it, int lane, u32x4 (&R)[kU]) {
-  const bool live = it.mode() != 0;
-  const Rsrc rt = row_rsrc(P.target, live ? it.r() : 0, P.tstride_b, live ? P.V * Fmt<DT>::ESIZE : 0);
-  issue_row<DT, VEC>(rt, it.c(), lane, R);
+  if (!VEC && !NOW) return;
+  issue_row<DT, VEC>(chunk_rsrc(P.target, it.r(), P.tstride_b, it.c(), P.V * Fmt<DT>::ESIZE, it.mode() != 0),
+                     lane, R);
 }
 
 // Phase 1 of a sampled row: chunk max, exponentials in place, chunk sum.
@@ -646,34 +724,6 @@ __device__ __forceinline__ void p1_row(float (&x)[Fmt<DT>::L], float s, float& m
   for (int k = 0; k < Fmt<DT>::L; ++k) {
     x[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k], s, c));
     a += x[k];
-  }
-  sum = wave_sum(a);
-}
-
-// The statistics p1_row computes for chunk c of a row, read again from
-// memory one vector at a time (few registers; a rare path): the same
-// operations on the same values in the same order, hence the same bits.
-template <int DT, bool VEC>
-__device__ __forceinline__ void stats_mem(Rsrc rs, int c, int V, int lane, float s, float& m, float& sum) {
-  using F = Fmt<DT>;
-  const int lim0 = V - (c * F::CH + lane * F::EPV);
-  float mm = -__builtin_huge_valf();
-#pragma unroll 1
-  for (int u = 0; u < kU; ++u) {
-    const u32x4 w = load_vec<DT, VEC>(rs, c, u, lane);
-    const int lim = lim0 - u * 64 * F::EPV;
-#pragma unroll
-    for (int e = 0; e < F::EPV; ++e) mm = fmaxf(mm, elem<DT>(w, e, lim));
-  }
-  m = wave_max(mm);
-  const float off = chunk_offset(m, s);
-  float a = 0.0f;
-#pragma unroll 1
-  for (int u = 0; u < kU; ++u) {
-    const u32x4 w = load_vec<DT, VEC>(rs, c, u, lane);
-    const int lim = lim0 - u * 64 * F::EPV;
-#pragma unroll
-    for (int e = 0; e < F::EPV; ++e) a += __builtin_amdgcn_exp2f(__builtin_fmaf(elem<DT>(w, e, lim), s, off));
   }
   sum = wave_sum(a);
 }
@@ -711,10 +761,14 @@ __device__ __forceinline__ void greedy_row(const float (&x)[Fmt<DT>::L], int c, 
 // D false: the launch has no draft logits; only row 0 exists.  `x` (D
 // false, sampled rows): a drafted token; if this chunk holds it, slot 2
 // carries e_t at x instead of the absent draft's maximum.
-template <int DT, bool D = true>
+template <int DT, bool VEC, bool D = true>
 __device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lane, uint64_t* wdummy,
-                                        const u32x4 (&R)[2][kU], float (&E)[2][Fmt<DT>::L], float& mt,
+                                        u32x4 (&R)[2][kU], float (&E)[2][Fmt<DT>::L], float& mt,
                                         float& md, float& st, int x = -1) {
+  if (!VEC) {   // element loads: issued here, not prefetched
+    if (D) issue_item<DT, VEC, true>(P, it, lane, R);
+    else issue_target<DT, VEC, true>(P, it, lane, R[0]);
+  }
   unpack<DT>(R[0], E[0]);
   if (D) unpack<DT>(R[1], E[1]);
   uint32_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
@@ -757,15 +811,105 @@ __device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lan
   if (lane < kX1) slot_put(dst + lane, P.epoch, v);
 }
 
-// A wave that has polled long enough for the slots of its row computes the
+// ------------------------------------------------------------------ recomputation from memory (help)
+// What phase 1 and phase 2 compute for one chunk, read again from memory one
+// vector at a time (few registers; a rare path): the same operations on the
+// same values in the same order, hence the same bits.
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void stats_mem(Rsrc rs, int c, int V, int lane, float s, float& m, float& sum) {
+  using F = Fmt<DT>;
+  const int lim0 = V - (c * F::CH + lane * F::EPV);
+  float mm = -__builtin_huge_valf();
+#pragma unroll 1
+  for (int u = 0; u < kU; ++u) {
+    const u32x4 w = load_vec<DT, VEC>(rs, u, lane);
+    const int lim = lim0 - u * 64 * F::EPV;
+#pragma unroll
+    for (int e = 0; e < F::EPV; ++e) mm = fmaxf(mm, elem<DT>(w, e, lim));
+  }
+  m = wave_max(mm);
+  const float off = chunk_offset(m, s);
+  float a = 0.0f;
+#pragma unroll 1
+  for (int u = 0; u < kU; ++u) {
+    const u32x4 w = load_vec<DT, VEC>(rs, u, lane);
+    const int lim = lim0 - u * 64 * F::EPV;
+#pragma unroll
+    for (int e = 0; e < F::EPV; ++e) a += __builtin_amdgcn_exp2f(__builtin_fmaf(elem<DT>(w, e, lim), s, off));
+  }
+  sum = wave_sum(a);
+}
+template <int DT, bool VEC>
+__device__ __forceinline__ void greedy_mem(Rsrc rs, int c, int V, int lane, float& v, int& k, int& bad) {
+  using F = Fmt<DT>;
+  const int lim0 = V - (c * F::CH + lane * F::EPV);
+  float bv = -__builtin_huge_valf();
+  int slot = -1, b = 0;
+#pragma unroll 1
+  for (int u = 0; u < kU; ++u) {
+    const u32x4 w = load_vec<DT, VEC>(rs, u, lane);
+    const int lim = lim0 - u * 64 * F::EPV;
+#pragma unroll
+    for (int e = 0; e < F::EPV; ++e) {
+      const float y = elem<DT>(w, e, lim);
+      b |= (y != y) | (y == __builtin_huge_valf());
+      const bool up = y > bv;
+      bv = up ? y : bv;
+      slot = up ? u * F::EPV + e : slot;
+    }
+  }
+  int bk = slot < 0 ? 0x7FFFFFFF : token_of<DT>(c, slot, lane);
+  wave_argmax(bv, bk);
+  v = bv;
+  k = bk;
+  bad = __any(b);
+}
+// Phase 1's four slot values of chunk c of row r (see p1_item).
+template <int DT, bool VEC, bool D>
+__device__ __forceinline__ void slots_mem(const Params& P, int r, int rd, int mode, bool dlog, bool drafted, float s,
+                                          int c, int lane, uint32_t (&v)[kX1]) {
+  const int nb = P.V * Fmt<DT>::ESIZE;
+  const Rsrc rt = chunk_rsrc(P.target, r, P.tstride_b, c, nb, true);
+  const Rsrc rdr = chunk_rsrc(P.draft, rd, P.dstride_b, c, nb, dlog);
+  if (mode == 1) {
+    float mt, st, md = -__builtin_huge_valf(), sd = 0.0f;
+    stats_mem<DT, VEC>(rt, c, P.V, lane, s, mt, st);
+    if (D && dlog) stats_mem<DT, VEC>(rdr, c, P.V, lane, s, md, sd);
+    v[0] = __float_as_uint(mt);
+    v[1] = __float_as_uint(st);
+    v[2] = __float_as_uint(md);
+    v[3] = __float_as_uint(sd);
+    if (!D && drafted) {
+      const int x = ld_const(P.tokens, rd);
+      if (x >= 0 && x < P.V && x / Fmt<DT>::CH == c) {
+        float lx;
+        const char* row = P.target + (uint64_t)(uint32_t)r * P.tstride_b;
+        if (DT == SPECVERIFY_F32) lx = ld_const((const float*)row, x);
+        else lx = __uint_as_float((uint32_t)ld_const((const uint16_t*)row, x) << 16);
+        v[2] = __float_as_uint(__builtin_amdgcn_exp2f(__builtin_fmaf(lx, s, chunk_offset(mt, s))));
+      }
+    }
+  } else {
+    float vt, vd = -__builtin_huge_valf();
+    int kt, kd = 0x7FFFFFFF, bt, bd = 0;
+    greedy_mem<DT, VEC>(rt, c, P.V, lane, vt, kt, bt);
+    if (D && dlog) greedy_mem<DT, VEC>(rdr, c, P.V, lane, vd, kd, bd);
+    v[0] = __float_as_uint(vt);
+    v[1] = bt ? 0xFFFFFFFFu : (uint32_t)kt;
+    v[2] = __float_as_uint(vd);
+    v[3] = bd ? 0xFFFFFFFFu : (uint32_t)kd;
+  }
+}
+// A wave that has polled long enough for the slots of row r computes the
 // missing chunks' statistics itself (their owners may not even be running:
 // nothing guarantees that every workgroup of the grid is resident at once)
 // and publishes them; the owners later write the same bits.  The caller
 // polls again afterwards.
-template <int DT, bool VEC, int NPER>
-__device__ __forceinline__ void help_row(const Params& P, const Item& it, int lane, const RowSlots<NPER>& q) {
+template <int DT, bool VEC, bool D, int NPER>
+__device__ __forceinline__ void help_slots(const Params& P, int r, int rd, int mode, bool dlog, bool drafted, float s,
+                                        int lane, const RowSlots<NPER>& q) {
   const uint32_t tag = P.epoch;
-  uint64_t miss[NPER];   // the slots are not needed past these masks
 #pragma unroll
   for (int j = 0; j < NPER; ++j) {
     bool m = false;
@@ -773,26 +917,62 @@ __device__ __forceinline__ void help_row(const Params& P, const Item& it, int la
 #pragma unroll
       for (int k = 0; k < kX1; ++k) m |= slot_tag(q.w[j][k]) != tag;
     }
-    miss[j] = __ballot(m);
-  }
-  const int nb = P.V * Fmt<DT>::ESIZE;
-  const Rsrc rt = row_rsrc(P.target, it.r(), P.tstride_b, nb);
-  const Rsrc rd = row_rsrc(P.draft, it.rd(), P.dstride_b, nb);
-#pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    uint64_t mask = miss[j];
+    uint64_t mask = __ballot(m);
     while (mask) {
       const int c = __builtin_ctzll(mask) + 64 * j;
       mask &= mask - 1;
-      float mt, st, md, sd;
-      stats_mem<DT, VEC>(rt, c, P.V, lane, it.s, mt, st);
-      stats_mem<DT, VEC>(rd, c, P.V, lane, it.s, md, sd);
-      if (lane < kX1) {
-        float y = lane == 2 ? md : sd;
-        y = lane == 1 ? st : y;
-        const uint32_t x = __float_as_uint(lane == 0 ? mt : y);
-        slot_put(P.xch1 + ((int64_t)it.r() * P.C + c) * kX1 + lane, tag, x);
+      uint32_t v[kX1];
+      slots_mem<DT, VEC, D>(P, r, rd, mode, dlog, drafted, s, c, lane, v);
+      uint32_t y = lane == 2 ? v[2] : v[3];
+      y = lane == 1 ? v[1] : y;
+      y = lane == 0 ? v[0] : y;
+      if (lane < kX1) slot_put(P.xch1 + ((int64_t)r * P.C + c) * kX1 + lane, tag, y);
+    }
+  }
+}
+// The same for missing partials of a sampled row with draft logits, once its
+// slots are complete (in q): phase 2 of each missing chunk from memory.
+template <int DT, bool VEC, int NPER>
+__device__ __forceinline__ void help_parts(const Params& P, int r, int rd, float s, int lane, const RowSlots<NPER>& q,
+                                        const float4 (&pt)[NPER]) {
+  using F = Fmt<DT>;
+  const uint32_t tag = P.epoch;
+  float Mt, St, Md, Sd;
+  merge_row(q, P.C, 0, s, lane, Mt, St);
+  merge_row(q, P.C, 2, s, lane, Md, Sd);
+  const int nb = P.V * F::ESIZE;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    uint64_t mask = __ballot(lane + 64 * j < P.C && __float_as_uint(pt[j].x) != tag);
+    while (mask) {
+      const int l = __builtin_ctzll(mask);
+      const int c = l + 64 * j;
+      mask &= mask - 1;
+      const float mt = __int_as_float(__builtin_amdgcn_readlane((int)(uint32_t)q.w[j][0], l));
+      const float st = __int_as_float(__builtin_amdgcn_readlane((int)(uint32_t)q.w[j][1], l));
+      const float md = __int_as_float(__builtin_amdgcn_readlane((int)(uint32_t)q.w[j][2], l));
+      const float rho = chunk_rho(mt, Mt, St, md, Md, Sd, s);
+      const float ct = chunk_offset(mt, s), cd = chunk_offset(md, s);
+      const Rsrc rt = chunk_rsrc(P.target, r, P.tstride_b, c, nb, true);
+      const Rsrc rdr = chunk_rsrc(P.draft, rd, P.dstride_b, c, nb, true);
+      const int lim0 = P.V - (c * F::CH + lane * F::EPV);
+      float b = 0.0f;
+#pragma unroll 1
+      for (int u = 0; u < kU; ++u) {
+        const u32x4 wt = load_vec<DT, VEC>(rt, u, lane);
+        const u32x4 wd = load_vec<DT, VEC>(rdr, u, lane);
+        const int lim = lim0 - u * 64 * F::EPV;
+#pragma unroll
+        for (int e = 0; e < F::EPV; ++e) {
+          const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<DT>(wt, e, lim), s, ct));
+          const float ed = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<DT>(wd, e, lim), s, cd));
+          b += min_nonneg(et, rho * ed);
+        }
       }
+      const float bs = wave_sum(b);
+      if (lane == 0)
+        *(float4*)(P.part + ((int64_t)r * P.C + c) * kPart) =
+            make_float4(__uint_as_float(tag), fmaxf(st - bs, 0.0f), bs, 0.0f);
     }
   }
 }
@@ -809,22 +989,22 @@ __device__ __forceinline__ void p2_item(const Params& P, const Item& it, int lan
   if (!ready) {
     for (int k = 0;; ++k) {
       // the help makes the next poll succeed; the bound only guards that
-      if (k > 2 * P.spin_limit + 16) return;   // no completion mark: the finisher reports it
+      if (k > 2 * P.spin_limit + 16) return;   // no partials: the resolution reports it
       if (k == P.spin_limit) {
-        help_row<DT, VEC, NPER>(P, it, lane, q);
+        help_slots<DT, VEC, true, NPER>(P, it.r(), it.rd(), 1, true, true, it.s, lane, q);
         __builtin_amdgcn_s_waitcnt(0);   // its stores are in L2 before the poll below
       } else {
         __builtin_amdgcn_s_sleep(2);
       }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the loads below are read again on every turn
       slots_issue(P, it.r(), true, soff, q);
-      if (slots_ready(q, P.C, tag, kX1, lane)) break;
+      if (slots_ready(q, P.C, tag, lane)) break;
     }
   }
   float Mt, St, Md, Sd;
   merge_row(q, P.C, 0, it.s, lane, Mt, St);
   merge_row(q, P.C, 2, it.s, lane, Md, Sd);
-  // invalid data gives NaN or inf here; the finisher checks the normalisers
+  // invalid data gives NaN or inf here; the resolution checks the normalisers
   const float rho = chunk_rho(mt, Mt, St, md, Md, Sd, it.s);   // q_k = a_t rho e_d
   // sum of min(e_t, rho e_d); the residual's sum is the chunk sum of e_t
   // (phase 1's st, the same values added in the same order) minus it
@@ -846,8 +1026,7 @@ __device__ __forceinline__ void p2_item(const Params& P, const Item& it, int lan
 // phase 1, so that the other chunks of its row have mostly published by
 // then.  Vector memory operations complete in order, so waiting for it also
 // waits for n2's loads, issued a step earlier: those are needed next step
-// anyway.  (Issuing the poll a step earlier, before n3's loads, measured
-// 1 us slower per launch: it more often found the row incomplete.)
+// anyway.
 // Every path through a step issues the same memory operations (items that
 // do not exist read zero-sized buffers and write the dummy slots), so the
 // compiler's count of operations in flight is exact at every wait.
@@ -858,13 +1037,12 @@ __device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy
                                      float cst, const Item& n1, u32x4 (&R1)[2][kU], float (&Efree)[2][Fmt<DT>::L],
                                      float& nmt, float& nmd, float& nst, const Item& n3) {
   // Phase 1 publishes what other waves' phase 2 polls for: it runs at a
-  // higher issue priority than the other wave of its SIMD (1.2 us faster per
-  // launch than equal priorities).
+  // higher issue priority than the other waves of its SIMD.
   __builtin_amdgcn_s_setprio(3);
-  p1_item<DT>(P, n1, lane, wdummy, R1, Efree, nmt, nmd, nst);
+  p1_item<DT, VEC>(P, n1, lane, wdummy, R1, Efree, nmt, nmd, nst);
   __builtin_amdgcn_s_setprio(0);
   slots_issue(P, cur.r(), cur.mode() == 1 && cur.pair(), soff, q);
-  const bool ready = slots_ready(q, P.C, P.epoch, kX1, lane);   // consumes the poll on every path
+  const bool ready = slots_ready(q, P.C, P.epoch, lane);   // consumes the poll on every path
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float* dst = (float*)(wdummy + kX1);
   if (cur.mode() == 1 && cur.pair()) p2_item<DT, VEC, NPER>(P, cur, lane, soff, q, ready, Ecur, cmt, cmd, cst, o, dst);
@@ -874,91 +1052,7 @@ __device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int DT, bool VEC, int NPER>
-__global__ __launch_bounds__(kStreamThreads, 2) void stream_kernel(Params P) {
-  using F = Fmt<DT>;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = (int)(blockIdx.x % kGroups);
-  const int j = (int)(blockIdx.x / kGroups) * kStreamWaves + wave;
-  const int n_items = ((P.R_t - grp + kGroups - 1) / kGroups) * P.C;
-  if (j >= n_items) return;
-  const int G = P.Gw;
-  uint32_t soff[NPER];
-  slot_offsets(P.C, lane, soff);
-  // the wave's own dummy slots: waves never contend for a dummy cache line
-  uint64_t* wdummy = P.dummy + ((int64_t)blockIdx.x * kStreamWaves + wave) * 8;
-
-  u32x4 RA[2][kU], RB[2][kU];
-  float EA[2][F::L], EB[2][F::L];
-  float amt = 0.0f, amd = 0.0f, ast = 0.0f, bmt = 0.0f, bmd = 0.0f, bst = 0.0f;
-  RowSlots<NPER> q;
-  // prologue: items 0 and 1 in flight, phase 1 of item 0, item 2 in flight
-  Item ia = make_item(P, grp, j, n_items);
-  Item ib = make_item(P, grp, j + G, n_items);
-  issue_item<DT, VEC>(P, ia, lane, RA);
-  __builtin_amdgcn_sched_barrier(0);
-  issue_item<DT, VEC>(P, ib, lane, RB);
-  __builtin_amdgcn_sched_barrier(0);
-  p1_item<DT>(P, ia, lane, wdummy, RA, EA, amt, amd, ast);
-  __builtin_amdgcn_sched_barrier(0);
-  Item ic = make_item(P, grp, j + 2 * G, n_items);
-  issue_item<DT, VEC>(P, ic, lane, RA);
-  __builtin_amdgcn_sched_barrier(0);
-  // Two steps per turn, one exit at the top: when the first step's item is
-  // the wave's last, the second step runs on nothing (no waits, dummy writes).
-  for (int idx = j; idx < n_items; idx += 2 * G) {
-    // cur = ia (EA), n1 = ib (RB), n2 = ic (RA, in flight)
-    const Item id = make_item(P, grp, idx + 3 * G, n_items);
-    step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ia, EA, amt, amd, ast, ib, RB, EB, bmt, bmd, bst, id);
-    // cur = ib (EB), n1 = ic (RA), n2 = id (RB, in flight)
-    const Item ie = make_item(P, grp, idx + 4 * G, n_items);
-    step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ib, EB, bmt, bmd, bst, ic, RA, EA, amt, amd, ast, ie);
-    ia = ic;
-    ib = id;
-    ic = ie;
-  }
-  // loads of items past the end read zero-sized buffers; let them land
-  __builtin_amdgcn_s_waitcnt(0);
-}
-
-// The streaming pass of a launch without draft logits (token-only drafts,
-// or gamma = 0 everywhere): phase 1 alone, one item per wave.  No item reads
-// another's statistics, so nothing waits on other waves and the grid need
-// not be resident at once: it covers every item, and the dispatcher starts
-// new waves as others end (measured faster than persistent waves with one to
-// four items in flight each).
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kStreamThreads) void stream_t_kernel(Params P) {
-  using F = Fmt<DT>;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = (int)(blockIdx.x % kGroups);
-  const int j = (int)(blockIdx.x / kGroups) * kStreamWaves + wave;
-  const int n_items = ((P.R_t - grp + kGroups - 1) / kGroups) * P.C;
-  if (j >= n_items) return;
-  const Item it = make_item(P, grp, j, n_items);
-  if (it.mode() == 0) return;   // nothing to read or publish
-  u32x4 R[2][kU];               // row 1 is never loaded or read
-  float E[2][F::L];
-  issue_target<DT, VEC>(P, it, lane, R[0]);
-  // a token-only draft x of this row: the chunk that holds it also publishes
-  // e_t at x (slot 2, unused without draft logits), so that the finish needs
-  // no dependent read of the logit at x
-  int x = -1;
-  if (P.token_only && it.mode() == 1) {
-    const RowMeta m = row_meta(P, it.r());
-    if (m.pair) x = ld_const(P.tokens, m.rd);
-  }
-  float mt, md, st;
-  p1_item<DT, false>(P, it, lane, P.dummy, R, E, mt, md, st, x);
-}
-
-// ================================================================== finish kernel
-
-struct FinishShared {
-  uint32_t res[kMaxGamma + 1];   // row results of the sequence
-};
+// ================================================================== resolution of a sequence
 
 __device__ __forceinline__ uint32_t row_payload(int status, bool acc, int tok) {
   return ((uint32_t)status << kStatusShift) | (acc ? kAccBit : 0u) |
@@ -976,68 +1070,65 @@ __device__ __forceinline__ float pick(const float (&a)[NPER], int j) {
 
 // One logit of a row as fp32 (token t < V).
 template <int DT>
-__device__ __forceinline__ float load_logit(const char* base, int64_t row, int64_t stride_b, int t) {
-  const char* p = base + row * stride_b;
+__device__ __forceinline__ float load_logit(const char* base, int row, uint32_t stride_b, int t) {
+  const char* p = base + (uint64_t)(uint32_t)row * stride_b;
   if (DT == SPECVERIFY_F32) return ((const float*)p)[t];
   return __uint_as_float((uint32_t)((const uint16_t*)p)[t] << 16);
 }
 
-// What a row's resolution reads first: its chunk slots, its partials and
-// the drafted token.  finish_kernel issues these before the row's
-// temperature is known, so that their latency overlaps the scalar loads.
+// What a row's resolution reads: its chunk slots, its partials (rows with
+// draft logits) and the drafted token.
 template <int NPER>
 struct RowIn {
   RowSlots<NPER> q;
-  float4 pt[NPER];   // {tag, W_c, B_c} of the lane's chunks (rows with draft logits)
+  float4 pt[NPER];   // {tag, W_c, B_c} of the lane's chunks
   int x;             // drafted token (rows with a draft)
 };
-template <int NPER>
-__device__ __forceinline__ void row_loads(const Params& P, int r, int rd, bool pair, int lane, RowIn<NPER>& in) {
-  uint32_t soff[NPER];
-  slot_offsets(P.C, lane, soff);
-  slots_issue(P, r, true, soff, in.q);
-  const bool dp = pair && !P.token_only;
-#pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    const int c = lane + 64 * j;
-    in.pt[j] = (dp && c < P.C) ? *(const float4*)(P.part + ((int64_t)r * P.C + c) * kPart)
-                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  }
-  in.x = pair ? ld_const(P.tokens, rd) : 0;
-}
 
-// One row of a sampled sequence, on one wave.  Returns the row result.
+// The final sample of a row, prepared while the row is resolved and
+// finished once the sequence's first rejection is known: the chunk whose
+// CDF interval holds the threshold (its logits are re-read right away), and
+// what the scan of that chunk in token order needs.
+struct SampleJob {
+  int row;       // row index j in the sequence; -1: none
+  int cs;        // owner chunk
+  float tau;     // threshold, in the chunk's units, less the mass before the chunk
+  float rho, ct, cd;
+  int x;         // the drafted token (removed from a token-only residual)
+  bool resid;    // weights of the residual max(0, p - q); otherwise of p
+  bool tk;       // token-only draft: the residual is p without x
+};
+
+// Phase A of one sampled row, on one wave, once its slots (and partials)
+// are complete: p(x), q(x), beta, Z; the acceptance test u_i q(x) < p(x);
+// and, for the wave's first row that needs the final sample (a rejected
+// draft, or the bonus row), the owner chunk, whose logits are loaded into R.
+// Returns the row result (accepted rows carry their draft token).
 template <int DT, bool VEC, int NPER>
-__device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int rd, bool pair, float T, float ui,
-                                                   float ug, int lane, const RowIn<NPER>& in) {
+__device__ __forceinline__ uint32_t accept_sampled(const Params& P, int j, int r, int rd, bool pair, bool dp, float T,
+                                                   float ui, float ug, int lane, const RowIn<NPER>& in, SampleJob& job,
+                                                   u32x4 (&R)[2][kU]) {
   using F = Fmt<DT>;
   const int C = P.C;
-  const uint32_t tag = P.epoch;
   const float s = kLog2e / T;
   const float ninf = -__builtin_huge_valf();
   // dp: the draft's logits are there; tk: a token-only draft, q = delta_x
-  const bool dp = pair && !P.token_only, tk = pair && P.token_only;
+  const bool tk = pair && !dp;
   const int x = in.x;
   const bool x_ok = x >= 0 && x < P.V;
   const RowSlots<NPER>& q = in.q;
   float W[NPER], Bp[NPER];
-  int done = 1;
 #pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    W[j] = 0.0f;
-    Bp[j] = 0.0f;
-    if (dp && lane + 64 * j < C) {
-      done &= __float_as_uint(in.pt[j].x) == tag;
-      W[j] = in.pt[j].y;
-      Bp[j] = in.pt[j].z;
-    }
+  for (int jj = 0; jj < NPER; ++jj) {
+    const bool inr = dp && lane + 64 * jj < C;
+    W[jj] = inr ? in.pt[jj].y : 0.0f;
+    Bp[jj] = inr ? in.pt[jj].z : 0.0f;
   }
   float lx = 0.0f, dx = 0.0f;
   if (dp && x_ok) {   // token-only rows read e_t at x from the slots instead
     lx = load_logit<DT>(P.target, r, P.tstride_b, x);
     dx = load_logit<DT>(P.draft, rd, P.dstride_b, x);
   }
-  if (!slots_ready(q, C, tag, dp ? 4 : 2, lane) || !__all(done)) return row_payload(2, false, 0);
   float Mt, St, Md = ninf, Sd = 0.0f;
   merge_row(q, C, 0, s, lane, Mt, St);
   if (dp) merge_row(q, C, 2, s, lane, Md, Sd);
@@ -1047,27 +1138,24 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
   // per-chunk scales, residual mass, beta, and the masses the final sample reads
   float at[NPER], tot[NPER], mt[NPER], md[NPER], rho[NPER];
 #pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    const bool in = lane + 64 * j < C;
-    mt[j] = in ? slot_f(q.w[j][0]) : ninf;
-    md[j] = (in && dp) ? slot_f(q.w[j][2]) : ninf;
-    at[j] = in ? chunk_scale(mt[j], Mt, St, s) : 0.0f;
-    rho[j] = (in && dp) ? chunk_rho(mt[j], Mt, St, md[j], Md, Sd, s) : 0.0f;
+  for (int jj = 0; jj < NPER; ++jj) {
+    const bool inr = lane + 64 * jj < C;
+    mt[jj] = inr ? slot_f(q.w[jj][0]) : ninf;
+    md[jj] = (inr && dp) ? slot_f(q.w[jj][2]) : ninf;
+    at[jj] = inr ? chunk_scale(mt[jj], Mt, St, s) : 0.0f;
+    rho[jj] = (inr && dp) ? chunk_rho(mt[jj], Mt, St, md[jj], Md, Sd, s) : 0.0f;
   }
   const float mtx = lane_f(pick(mt, jx), lxl);
   // e at x as phase 1 computed it (the same operations on the same values);
   // for a token-only draft phase 1 published it in slot 2 of x's chunk
   float ex;
   if (tk) {
-    uint32_t tgx = 0, vx = 0;   // slot 2 of chunk cx, read from its lane
+    uint32_t vx = 0;   // slot 2 of chunk cx, read from its lane
 #pragma unroll
-    for (int j = 0; j < NPER; ++j) {
-      const uint32_t tj = (uint32_t)__builtin_amdgcn_readlane((int)slot_tag(q.w[j][2]), lxl);
-      const uint32_t vj = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)q.w[j][2], lxl);
-      tgx = j == jx ? tj : tgx;
-      vx = j == jx ? vj : vx;
+    for (int jj = 0; jj < NPER; ++jj) {
+      const uint32_t vj = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)q.w[jj][2], lxl);
+      vx = jj == jx ? vj : vx;
     }
-    if (tgx != tag) return row_payload(2, false, 0);   // not published: internal error
     ex = __uint_as_float(vx);
   } else {
     ex = __builtin_amdgcn_exp2f(__builtin_fmaf(lx, s, chunk_offset(mtx, s)));
@@ -1076,78 +1164,24 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
     // the residual p - delta_x is p without x: the chunk sums of e_t, less
     // x's own e in its chunk
 #pragma unroll
-    for (int j = 0; j < NPER; ++j) {
-      const bool in = lane + 64 * j < C;
-      W[j] = in ? slot_f(q.w[j][1]) : 0.0f;
-      if (lane + 64 * j == cx) W[j] = fmaxf(W[j] - ex, 0.0f);
+    for (int jj = 0; jj < NPER; ++jj) {
+      const bool inr = lane + 64 * jj < C;
+      W[jj] = inr ? slot_f(q.w[jj][1]) : 0.0f;
+      if (lane + 64 * jj == cx) W[jj] = fmaxf(W[jj] - ex, 0.0f);
     }
   }
   float zl = 0.0f, bl = 0.0f;
 #pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    const bool in = lane + 64 * j < C;
-    zl += in ? at[j] * W[j] : 0.0f;
-    bl += in ? at[j] * Bp[j] : 0.0f;
+  for (int jj = 0; jj < NPER; ++jj) {
+    const bool inr = lane + 64 * jj < C;
+    zl += inr ? at[jj] * W[jj] : 0.0f;
+    bl += inr ? at[jj] * Bp[jj] : 0.0f;
   }
   float Z = 0.0f, beta = 0.0f;
   if (pair) {
     Z = wave_sum(zl);
     beta = wave_sum(bl);
   }
-  const bool resid = pair && Z > 0.0f;
-  float ml = 0.0f;
-#pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    const bool in = lane + 64 * j < C;
-    tot[j] = !in ? 0.0f : resid ? at[j] * W[j] : at[j] * slot_f(q.w[j][1]);
-    ml += tot[j];
-  }
-  const float mass = resid ? Z : wave_sum(ml);
-  const float thr = ug * mass;
-  // the owner chunk: first chunk whose cumulative mass exceeds thr (chunks
-  // with zero mass never own); rounding guard: the last chunk with mass
-  int cs = -1, last = -1;
-  float before = 0.0f, last_before = 0.0f, base = 0.0f;
-#pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    const bool in = lane + 64 * j < C;
-    const float t = in ? tot[j] : 0.0f;
-    const float G = base + wave_scan(t, lane);
-    const float Gex = G - t;
-    const uint64_t hit = __ballot(in && t > 0.0f && G > thr);
-    const uint64_t pos = __ballot(in && t > 0.0f);
-    if (cs < 0 && hit) {
-      const int l = __builtin_ctzll(hit);
-      cs = 64 * j + l;
-      before = lane_f(Gex, l);
-    }
-    if (pos) {
-      const int l = 63 - __builtin_clzll(pos);
-      last = 64 * j + l;
-      last_before = lane_f(Gex, l);
-    }
-    base = lane_f(G, 63);
-  }
-  if (cs < 0) {
-    cs = last;
-    before = last_before;
-  }
-  const bool no_owner = cs < 0;   // unreachable for a valid row
-  if (no_owner) cs = 0;
-  const int ls = cs & 63, js = cs >> 6;
-  const float a_s = lane_f(pick(at, js), ls);
-  const float rho_s = lane_f(pick(rho, js), ls);
-  const float ct = chunk_offset(lane_f(pick(mt, js), ls), s);
-  const float cd = chunk_offset(lane_f(pick(md, js), ls), s);
-  // re-read the owner chunk and scan its weights in token order
-  const int nb = P.V * F::ESIZE;
-  u32x4 R[2][kU];
-  issue_row<DT, VEC>(row_rsrc(P.target, r, P.tstride_b, nb), cs, lane, R[0]);
-  const bool rd_read = resid && dp;
-  issue_row<DT, VEC>(row_rsrc(P.draft, rd_read ? rd : 0, P.dstride_b, rd_read ? nb : 0), cs, lane, R[1]);
-  // The owner chunk needs only the slots and partials (and, for a token-only
-  // draft, x's logit): its loads go out before the acceptance test, whose
-  // logits at x may still be in flight.
   // p(x), q(x): the logits at x with their chunk's offset and scale; the
   // acceptance test u q(x) < p(x)
   if (pair) {
@@ -1161,25 +1195,82 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
       if (P.beta) P.beta[rd] = beta;
       if (P.resid) P.resid[rd] = Z;
     }
-    // an accepted draft emits itself: its row's residual token is never used
-    // (the owner chunk's loads land before the wave goes on)
-    if (ui * qx < px) {
-      __builtin_amdgcn_s_waitcnt(0);
-      return row_payload(0, true, x);   // an accepted row emits its draft
-    }
+    if (ui * qx < px) return row_payload(0, true, x);   // an accepted draft emits itself
   }
-  if (no_owner) return row_payload(2, false, 0);
+  if (job.row >= 0) return row_payload(0, false, 0);   // an earlier row of this wave needs the sample
+  // The final sample: the owner chunk is the first chunk whose cumulative
+  // mass exceeds thr = u_gamma * mass (chunks with zero mass never own);
+  // rounding guard: the last chunk with mass.
+  const bool resid = pair && Z > 0.0f;
+  float ml = 0.0f;
+#pragma unroll
+  for (int jj = 0; jj < NPER; ++jj) {
+    const bool inr = lane + 64 * jj < C;
+    tot[jj] = !inr ? 0.0f : resid ? at[jj] * W[jj] : at[jj] * slot_f(q.w[jj][1]);
+    ml += tot[jj];
+  }
+  const float mass = resid ? Z : wave_sum(ml);
+  const float thr = ug * mass;
+  int cs = -1, last = -1;
+  float before = 0.0f, last_before = 0.0f, base = 0.0f;
+#pragma unroll
+  for (int jj = 0; jj < NPER; ++jj) {
+    const bool inr = lane + 64 * jj < C;
+    const float t = inr ? tot[jj] : 0.0f;
+    const float Gs = base + wave_scan(t, lane);
+    const float Gex = Gs - t;
+    const uint64_t hit = __ballot(inr && t > 0.0f && Gs > thr);
+    const uint64_t pos = __ballot(inr && t > 0.0f);
+    if (cs < 0 && hit) {
+      const int l = __builtin_ctzll(hit);
+      cs = 64 * jj + l;
+      before = lane_f(Gex, l);
+    }
+    if (pos) {
+      const int l = 63 - __builtin_clzll(pos);
+      last = 64 * jj + l;
+      last_before = lane_f(Gex, l);
+    }
+    base = lane_f(Gs, 63);
+  }
+  if (cs < 0) {
+    cs = last;
+    before = last_before;
+  }
+  if (cs < 0) return row_payload(2, false, 0);   // unreachable for a valid row
+  const int ls = cs & 63, js = cs >> 6;
+  job.row = j;
+  job.cs = cs;
+  job.tau = (thr - before) / lane_f(pick(at, js), ls);
+  job.rho = lane_f(pick(rho, js), ls);
+  job.ct = chunk_offset(lane_f(pick(mt, js), ls), s);
+  job.cd = chunk_offset(lane_f(pick(md, js), ls), s);
+  job.x = x;
+  job.resid = resid;
+  job.tk = tk;
+  // re-read the owner chunk now: its loads land while the other rows resolve
+  const int nb = P.V * F::ESIZE;
+  issue_row<DT, VEC>(chunk_rsrc(P.target, r, P.tstride_b, cs, nb, true), lane, R[0]);
+  issue_row<DT, VEC>(chunk_rsrc(P.draft, rd, P.dstride_b, cs, nb, resid && dp), lane, R[1]);
+  return row_payload(0, false, 0);
+}
+
+// Phase B: the token of a prepared sample, from the re-read owner chunk in R.
+// Running sums in the chunk's units against tau.  Token order inside the
+// chunk is round u (one 16-byte vector per lane), then lane, then element.
+// Per round: the weights (recomputed with the same functions as phase 2,
+// one branch per row around straight-line code), a wave scan of the lane
+// sums and the first position whose running sum exceeds tau.  Rounds go in
+// order and stop at the first with a hit.  Returns the token, or -1.
+template <int DT>
+__device__ __forceinline__ int sample_scan(const Params& P, const SampleJob& job, float s, int lane,
+                                           u32x4 (&R)[2][kU]) {
+  using F = Fmt<DT>;
+  const int cs = job.cs;
   if ((cs + 1) * F::CH > P.V) {   // tokens >= V: weight 0
     mask_raw<DT>(R[0], cs, P.V, lane);
     mask_raw<DT>(R[1], cs, P.V, lane);
   }
-  // Running sums in the chunk's units against tau = (thr - before) / a_s.
-  // Token order inside the chunk is round u (one 16-byte vector per lane),
-  // then lane, then element.  Per round: the weights (recomputed with the
-  // same functions as phase 2, one branch per row around straight-line
-  // code), a wave scan of the lane sums and the first position whose running
-  // sum exceeds tau.  Rounds go in order and stop at the first with a hit.
-  const float tau = (thr - before) / a_s;
   int first = 0x7FFFFFFF, lastpos = -1;
   float rbase = 0.0f;
 #pragma unroll 1
@@ -1192,20 +1283,20 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
       vd = i == u ? R[1][i] : vd;
     }
     float w[F::EPV];
-    if (tk && resid) {
+    if (job.tk && job.resid) {
 #pragma unroll
       for (int e = 0; e < F::EPV; ++e) {   // p without x
-        const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vt, e), s, ct));
-        w[e] = token_of<DT>(cs, u * F::EPV + e, lane) == x ? 0.0f : et;
+        const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vt, e), s, job.ct));
+        w[e] = token_of<DT>(cs, u * F::EPV + e, lane) == job.x ? 0.0f : et;
       }
-    } else if (resid) {
+    } else if (job.resid) {
 #pragma unroll
       for (int e = 0; e < F::EPV; ++e)
-        w[e] = resid_w(__builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vt, e), s, ct)),
-                       __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vd, e), s, cd)), rho_s);
+        w[e] = resid_w(__builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vt, e), s, job.ct)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vd, e), s, job.cd)), job.rho);
     } else {
 #pragma unroll
-      for (int e = 0; e < F::EPV; ++e) w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vt, e), s, ct));
+      for (int e = 0; e < F::EPV; ++e) w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vt, e), s, job.ct));
     }
     float loc[F::EPV];
     float run = 0.0f;
@@ -1221,7 +1312,7 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
     for (int e = F::EPV - 1; e >= 0; --e) {
       const int k = u * 64 * F::EPV + lane * F::EPV + e;   // position inside the chunk
       if (w[e] > 0.0f) {
-        if (excl + loc[e] > tau) cand = k;
+        if (excl + loc[e] > job.tau) cand = k;
         lastpos = max(lastpos, k);
       }
     }
@@ -1233,22 +1324,16 @@ __device__ __forceinline__ uint32_t finish_sampled(const Params& P, int r, int r
   }
   if (first == 0x7FFFFFFF) lastpos = wave_max_i(lastpos);   // every round was scanned
   const int pickk = first != 0x7FFFFFFF ? first : lastpos;
-  if (pickk < 0) return row_payload(2, false, 0);   // unreachable: the chunk has weight > 0
   const int tok = cs * F::CH + pickk;
-  if (tok >= P.V) return row_payload(2, false, 0);
-  return row_payload(0, false, tok);
+  return (pickk < 0 || tok >= P.V) ? -1 : tok;   // unreachable: the chunk has weight > 0
 }
 
-// One row of a greedy sequence, on one wave.
+// One row of a greedy sequence, on one wave, once its slots are complete.
 template <int NPER>
-__device__ __forceinline__ uint32_t finish_greedy(const Params& P, int r, int rd, bool pair, int lane,
+__device__ __forceinline__ uint32_t finish_greedy(const Params& P, int rd, bool pair, bool dp, int lane,
                                                   const RowIn<NPER>& in) {
   const int C = P.C;
-  const uint32_t tag = P.epoch;
-  // dp: the draft's logits are there; a token-only draft's argmax is x itself
-  const bool dp = pair && !P.token_only;
   const RowSlots<NPER>& q = in.q;
-  if (!slots_ready(q, C, tag, dp ? 4 : 2, lane)) return row_payload(2, false, 0);
   float av = -__builtin_huge_valf(), dv = -__builtin_huge_valf();
   int ak = 0x7FFFFFFF, dk = 0x7FFFFFFF, bad = 0;
 #pragma unroll
@@ -1271,7 +1356,7 @@ __device__ __forceinline__ uint32_t finish_greedy(const Params& P, int r, int rd
   if (pair) {
     const int x = in.x;
     if (x < 0 || x >= P.V) return row_payload(1, false, 0);
-    if (!dp) dk = x;
+    if (!dp) dk = x;   // a token-only draft's argmax is x itself
     acc = (x == ak);
     if (lane == 0) {
       if (P.p_draft) P.p_draft[rd] = (x == ak) ? 1.0f : 0.0f;
@@ -1283,60 +1368,208 @@ __device__ __forceinline__ uint32_t finish_greedy(const Params& P, int r, int rd
   return row_payload(0, acc, ak);
 }
 
-template <int DT, bool VEC, int NPER>
-__global__ __launch_bounds__(64 * kFinishWaves) void finish_kernel(Params P) {
-  __shared__ FinishShared sh;
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // rows are wave-uniform
-  const int nw = blockDim.x >> 6;
+// Row j (row r) of a sequence: wait until its slots (and, for a sampled row
+// with draft logits, its partials) carry this run's tag -- computing what is
+// still missing after spin_limit polls -- then resolve it (phase A).
+// D: the launch has draft logits.
+template <int DT, bool VEC, bool D, int NPER>
+__device__ __forceinline__ uint32_t resolve_row(const Params& P, int j, int r, int rd, bool pair, float T, float ui,
+                                                float ug, int lane, SampleJob& job, u32x4 (&R)[2][kU]) {
+  const bool sampled = t_sampled(T);
+  if (!(sampled || T == 0.0f) || !u_ok(ui)) return row_payload(1, false, 0);
+  const bool dp = D && pair;                // the position's draft logits are read
+  const bool dpart = dp && sampled;         // it has partials
+  const float s = sampled ? kLog2e / T : 0.0f;
+  uint32_t soff[NPER], poff[NPER];
+  chunk_offsets(P.C, lane, kX1 * (int)sizeof(uint64_t), soff);
+  chunk_offsets(P.C, lane, kPart * (int)sizeof(float), poff);
+  RowIn<NPER> in;
+  in.x = pair ? ld_const(P.tokens, rd) : 0;
+  for (int k = 0;; ++k) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the loads below are read again on every turn
+    slots_issue(P, r, true, soff, in.q);
+    part_issue(P, r, dpart, poff, in.pt);
+    const bool sready = slots_ready(in.q, P.C, P.epoch, lane);
+    if (sready && (!dpart || parts_ready(in.pt, P.C, P.epoch, lane))) break;
+    // the help makes the next poll succeed; the bound only guards that
+    if (k > 2 * P.spin_limit + 16) return row_payload(2, false, 0);
+    if (k == P.spin_limit) {
+      if (!sready) {
+        help_slots<DT, VEC, D, NPER>(P, r, rd, sampled ? 1 : 2, dp, pair, s, lane, in.q);
+        __builtin_amdgcn_s_waitcnt(0);   // its stores are in L2 before the reads below
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        slots_issue(P, r, true, soff, in.q);
+      }
+      if (dpart && slots_ready(in.q, P.C, P.epoch, lane)) {
+        help_parts<DT, VEC, NPER>(P, r, rd, s, lane, in.q, in.pt);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+    } else {
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  if (sampled) return accept_sampled<DT, VEC, NPER>(P, j, r, rd, pair, dp, T, ui, ug, lane, in, job, R);
+  return finish_greedy<NPER>(P, rd, pair, dp, lane, in);
+}
+
+// Sequence b, by one workgroup.  Phase A: its waves resolve the rows (row j
+// on wave j mod kStreamWaves, in order), and each wave prepares the final
+// sample of its first row that needs one.  The row results meet in LDS.
+// Phase B: the first rejection n; the wave that holds row n (its first row
+// needing the sample, since every earlier row was accepted) scans the
+// re-read chunk and writes the accepted length and the n + 1 tokens.
+template <int DT, bool VEC, bool D, int NPER>
+__device__ __forceinline__ void resolve_sequence(const Params& P, int b, int lane, int wv, uint32_t* shres) {
   int d0, gam;
   if (P.cu_draft == nullptr) {
     d0 = b * P.gamma;
     gam = P.gamma;
   } else {
-    if (*P.layout != P.epoch * 2u) {   // cu_draft is not a layout: every sequence and token is invalid
-      if (threadIdx.x == 0) P.acc_len[b] = -1;
-      for (int t = b + P.B * (int)threadIdx.x; t < P.R_t; t += P.B * (int)blockDim.x) P.out_tokens[t] = -1;
-      return;
-    }
     d0 = ld_const(P.cu_draft, b);
     gam = ld_const(P.cu_draft, b + 1) - d0;
   }
   const int t0 = d0 + b;
   const float T = ld_const(P.temps, b);
-  const bool sampled = t_sampled(T);
-  const bool t_ok = sampled || T == 0.0f;
   const float ug = ld_const(P.uniforms, t0 + gam);
-  for (int j = wv; j <= gam; j += nw) {
-    const bool pair = j < gam;
-    const int r = t0 + j, rd = d0 + j;
-    RowIn<NPER> in;
-    row_loads(P, r, rd, pair, lane, in);
-    uint32_t res;
-    if (!t_ok) res = row_payload(1, false, 0);
-    else if (sampled) res = finish_sampled<DT, VEC, NPER>(P, r, rd, pair, T, ld_const(P.uniforms, r), ug, lane, in);
-    else res = finish_greedy<NPER>(P, r, rd, pair, lane, in);
-    if (lane == 0) sh.res[j] = res;
+  SampleJob job;
+  job.row = -1;
+  u32x4 R[2][kU];
+  for (int j = wv; j <= gam; j += kStreamWaves) {
+    const int r = t0 + j;
+    const uint32_t res = resolve_row<DT, VEC, D, NPER>(P, j, r, d0 + j, j < gam, T, ld_const(P.uniforms, r), ug,
+                                                       lane, job, R);
+    if (lane == 0) shres[j] = res;
   }
   __syncthreads();
-  if (wv != 0) return;
-  // first rejection n, accepted length and the n + 1 tokens
+  // first rejection n and the sequence's status
   int n = gam, st = 0;
   for (int j0 = 0; j0 <= gam; j0 += 64) {
     const int j = j0 + lane;
-    const uint32_t v = j <= gam ? sh.res[j] : 0u;
+    const uint32_t v = j <= gam ? shres[j] : 0u;
     st = max(st, wave_max_i((int)(v >> kStatusShift)));
     const uint64_t rb = __ballot(j < gam && !(v & kAccBit));
     if (n == gam && rb) n = j0 + __builtin_ctzll(rb);
   }
-  // rows up to n carry their emitted token: the draft when accepted, the
-  // residual or bonus token at n
-  for (int j0 = 0; j0 <= gam; j0 += 64) {
-    const int j = j0 + lane;
-    if (j <= gam) P.out_tokens[t0 + j] = (st == 0 && j <= n) ? (int)(sh.res[j] & kTokMask) : -1;
+  const bool sampled = t_sampled(T);
+  const int writer = (st == 0 && sampled) ? n % kStreamWaves : 0;
+  if (wv == writer) {
+    int tn = 0;
+    if (st == 0) {
+      if (sampled) {
+        // job.row == n here: every row of this wave before n was accepted
+        tn = job.row == n ? sample_scan<DT>(P, job, kLog2e / T, lane, R) : -1;
+        if (tn < 0) st = 2;   // unreachable
+      } else {
+        tn = (int)(shres[n] & kTokMask);   // greedy: the argmax
+      }
+    }
+    // rows before n emit their drafts, row n the sampled token
+    for (int j0 = 0; j0 <= gam; j0 += 64) {
+      const int j = j0 + lane;
+      if (j <= gam) P.out_tokens[t0 + j] = (st != 0 || j > n) ? -1 : j < n ? (int)(shres[j] & kTokMask) : tn;
+    }
+    if (lane == 0) P.acc_len[b] = st == 2 ? -2 : st == 1 ? -1 : n;
   }
-  if (lane == 0) P.acc_len[b] = st == 2 ? -2 : st == 1 ? -1 : n;
+  // the re-read of a wave whose sample was not needed lands before R is reused
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();   // shres is reused by the next sequence
+}
+
+// Every output -1: the batch layout (cu_draft) is invalid.
+__device__ __forceinline__ void invalid_batch(const Params& P) {
+  const int n = P.R_t > P.B ? P.R_t : P.B;
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < n; t += gridDim.x * blockDim.x) {
+    if (t < P.B) P.acc_len[t] = -1;
+    if (t < P.R_t) P.out_tokens[t] = -1;
+  }
+}
+
+// ================================================================== the kernel
+
+// D: the launch has draft logits (two-phase pipeline); otherwise phase 1
+// alone, with the next item's loads in flight.
+template <int DT, bool VEC, int NPER, bool D>
+__global__ __launch_bounds__(kStreamThreads, D ? 2 : 1) void verify_kernel(Params P) {
+  using F = Fmt<DT>;
+  __shared__ uint32_t shres[kMaxGamma + 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = (int)(blockIdx.x % kGroups);
+  const int wgl = (int)(blockIdx.x / kGroups);
+  if (P.gbounds != nullptr && ld_const(P.layout, 0) != P.epoch * 2u) {
+    invalid_batch(P);
+    return;
+  }
+  const Group Gr = group_of(P, grp);
+  const int n_items = (Gr.r1 - Gr.r0) * P.C;
+  const int j = wgl * kStreamWaves + wave;
+  const int G = P.Gw;
+  // the wave's own dummy slots: waves never contend for a dummy cache line
+  uint64_t* wdummy = P.dummy + ((int64_t)blockIdx.x * kStreamWaves + wave) * 8;
+  if (j < n_items) {
+    if (D) {
+      uint32_t soff[NPER];
+      chunk_offsets(P.C, lane, kX1 * (int)sizeof(uint64_t), soff);
+      u32x4 RA[2][kU], RB[2][kU];
+      float EA[2][F::L], EB[2][F::L];
+      float amt = 0.0f, amd = 0.0f, ast = 0.0f, bmt = 0.0f, bmd = 0.0f, bst = 0.0f;
+      RowSlots<NPER> q;
+      // prologue: items 0 and 1 in flight, phase 1 of item 0, item 2 in flight
+      Item ia = make_item(P, Gr.r0, j, n_items);
+      Item ib = make_item(P, Gr.r0, j + G, n_items);
+      issue_item<DT, VEC>(P, ia, lane, RA);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_item<DT, VEC>(P, ib, lane, RB);
+      __builtin_amdgcn_sched_barrier(0);
+      p1_item<DT, VEC>(P, ia, lane, wdummy, RA, EA, amt, amd, ast);
+      __builtin_amdgcn_sched_barrier(0);
+      Item ic = make_item(P, Gr.r0, j + 2 * G, n_items);
+      issue_item<DT, VEC>(P, ic, lane, RA);
+      __builtin_amdgcn_sched_barrier(0);
+      // Two steps per turn, one exit at the top: when the first step's item is
+      // the wave's last, the second step runs on nothing (no waits, dummy writes).
+      for (int idx = j; idx < n_items; idx += 2 * G) {
+        // cur = ia (EA), n1 = ib (RB), n2 = ic (RA, in flight)
+        const Item id = make_item(P, Gr.r0, idx + 3 * G, n_items);
+        step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ia, EA, amt, amd, ast, ib, RB, EB, bmt, bmd, bst, id);
+        // cur = ib (EB), n1 = ic (RA), n2 = id (RB, in flight)
+        const Item ie = make_item(P, Gr.r0, idx + 4 * G, n_items);
+        step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ib, EB, bmt, bmd, bst, ic, RA, EA, amt, amd, ast, ie);
+        ia = ic;
+        ib = id;
+        ic = ie;
+      }
+    } else {
+      u32x4 RA[2][kU], RB[2][kU];   // row 1 is never loaded or read
+      float E[2][F::L];
+      float mt, md, st;
+      Item ia = make_item(P, Gr.r0, j, n_items);
+      issue_target<DT, VEC>(P, ia, lane, RA[0]);
+      for (int idx = j; idx < n_items; idx += 2 * G) {
+        const Item ib = make_item(P, Gr.r0, idx + G, n_items);
+        issue_target<DT, VEC>(P, ib, lane, RB[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        int x = -1;   // a token-only draft of this row: the chunk that holds it publishes e_t at x
+        if (P.token_only && ia.mode() == 1 && ia.drafted()) x = ld_const(P.tokens, ia.rd());
+        p1_item<DT, VEC, false>(P, ia, lane, wdummy, RA, E, mt, md, st, x);
+        __builtin_amdgcn_sched_barrier(0);
+        ia = make_item(P, Gr.r0, idx + 2 * G, n_items);
+        issue_target<DT, VEC>(P, ia, lane, RA[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        x = -1;
+        if (P.token_only && ib.mode() == 1 && ib.drafted()) x = ld_const(P.tokens, ib.rd());
+        p1_item<DT, VEC, false>(P, ib, lane, wdummy, RB, E, mt, md, st, x);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // loads of items past the end read zero-sized buffers; let them land
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  // Resolution: sequence k of the group goes to workgroup Wg - 1 - (k mod Wg).
+  // The last workgroups of a group stream one item fewer per wave when the
+  // items do not divide evenly, so they finish streaming first.
+  const int nseq = Gr.s1 - Gr.s0;
+  for (int k = P.Wg - 1 - wgl; k < nseq; k += P.Wg) resolve_sequence<DT, VEC, D, NPER>(P, Gr.s0 + k, lane, wave, shres);
 }
 
 // ================================================================== commit kernel
@@ -1391,17 +1624,16 @@ __global__ __launch_bounds__(64 * kCommitWaves) void commit_kernel(CommitParams 
 
 typedef void (*KernelFn)(Params);
 struct Kernels {
-  KernelFn stream, stream_t, finish;   // stream_t: launches without draft logits
+  KernelFn with_draft, no_draft;   // no_draft: launches without draft logits
 };
 template <int DT, bool VEC>
 Kernels kernels_for(int nper) {
-  if (nper == 1) return {stream_kernel<DT, VEC, 1>, stream_t_kernel<DT, VEC>, finish_kernel<DT, VEC, 1>};
-  if (nper == 2) return {stream_kernel<DT, VEC, 2>, stream_t_kernel<DT, VEC>, finish_kernel<DT, VEC, 2>};
+  if (nper == 1) return {verify_kernel<DT, VEC, 1, true>, verify_kernel<DT, VEC, 1, false>};
+  if (nper == 2) return {verify_kernel<DT, VEC, 2, true>, verify_kernel<DT, VEC, 2, false>};
   // more than 128 chunks per row: fp32 only (the bf16 build would not fit
   // its registers)
-  if constexpr (DT == SPECVERIFY_F32)
-    return {stream_kernel<DT, VEC, 4>, stream_t_kernel<DT, VEC>, finish_kernel<DT, VEC, 4>};
-  return {nullptr, nullptr, nullptr};
+  if constexpr (DT == SPECVERIFY_F32) return {verify_kernel<DT, VEC, 4, true>, verify_kernel<DT, VEC, 4, false>};
+  return {nullptr, nullptr};
 }
 Kernels kernels_for(int dtype, bool vec, int nper) {
   if (dtype == SPECVERIFY_F32) return vec ? kernels_for<SPECVERIFY_F32, true>(nper) : kernels_for<SPECVERIFY_F32, false>(nper);
@@ -1427,7 +1659,7 @@ struct specverify_ctx {
   int chunks;
   int nper;
   int64_t rows;            // max target rows
-  int cap[2];              // stream workgroups resident at once: [element loads, vector loads]
+  int cap[2][2];           // workgroups resident at once: [vector loads][draft logits]
   void* ws;
   size_t ws_bytes;
   uint64_t* xch1;
@@ -1435,6 +1667,7 @@ struct specverify_ctx {
   float* part;
   int4* rowinfo;
   uint32_t* layout;
+  int32_t* gbounds;
   uint32_t epoch;
   int timing;              // recording events
   int trec;                // runs recorded since the measurement started
@@ -1470,35 +1703,34 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
     delete h;
     return SPECVERIFY_ERR_DEVICE;
   }
-  // Residency of the persistent stream grid: workgroups per CU times CUs.
-  // A row group needs at least C waves, so that the chunks of a row fall
-  // into one round or two consecutive ones and their waves meet in time.
+  // Residency of the persistent grids: workgroups per CU times CUs.  With
+  // draft logits a row group needs at least C waves, so that the chunks of a
+  // row fall into one round or two consecutive ones and their waves meet in
+  // time.  A kernel that spilled to scratch would make the runtime allocate
+  // scratch at its first launch and spill in its inner loop: such a build is
+  // refused rather than run.
   int cus = 0;
-  h->cap[0] = h->cap[1] = 0;
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cfg->device);
-  // A kernel that spilled to scratch would make the runtime allocate scratch
-  // at its first launch and spill in its inner loop: such a build is refused
-  // rather than run.  (The kernel without draft logits never waits
-  // on other waves: its grid is not persistent and needs no residency.)
   int capmax = 0;
-  for (int v = 0; v < 6 && e == hipSuccess; ++v) {
-    const Kernels K = kernels_for(cfg->dtype, (v & 1) == 1, h->nper);
-    const void* fn = (const void*)(v < 2 ? K.stream : v < 4 ? K.stream_t : K.finish);
+  for (int v = 0; v < 4 && e == hipSuccess; ++v) {
+    const bool vec = (v & 1) == 1, dl = v < 2;
+    const Kernels K = kernels_for(cfg->dtype, vec, h->nper);
+    const void* fn = (const void*)(dl ? K.with_draft : K.no_draft);
     hipFuncAttributes fa;
     e = hipFuncGetAttributes(&fa, fn);
     if (e == hipSuccess && fa.localSizeBytes > 0) e = hipErrorInvalidConfiguration;
-    if (v >= 2) continue;
     int per_cu = 0;
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStreamThreads, 0);
-    h->cap[v] = cus * per_cu;
-    if (h->cap[v] > capmax) capmax = h->cap[v];
-    if (e == hipSuccess && (h->cap[v] / kGroups) * kStreamWaves < C) e = hipErrorInvalidConfiguration;
+    h->cap[vec][dl] = cus * per_cu;
+    if (h->cap[vec][dl] > capmax) capmax = h->cap[vec][dl];
+    if (e == hipSuccess && (per_cu < 1 || (dl && (h->cap[vec][dl] / kGroups) * kStreamWaves < C)))
+      e = hipErrorInvalidConfiguration;
   }
   const size_t n1 = (size_t)rows * C * kX1 * sizeof(uint64_t);
-  const size_t nd = (size_t)capmax * kStreamWaves * 8 * sizeof(uint64_t);   // dummy slots, per stream wave
+  const size_t nd = (size_t)capmax * kStreamWaves * 8 * sizeof(uint64_t);   // dummy slots, per wave
   const size_t n2 = (size_t)rows * C * kPart * sizeof(float);
   const size_t n3 = (size_t)rows * sizeof(int4);
-  const size_t n4 = 256;                                   // layout flag
+  const size_t n4 = 256;                                   // layout flag and group bounds
   h->ws_bytes = n1 + nd + n2 + n3 + n4;
   void* p = nullptr;
   if (e == hipSuccess) e = hipMalloc(&p, h->ws_bytes);
@@ -1519,6 +1751,7 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
   h->part = (float*)(q + n1 + nd);
   h->rowinfo = (int4*)(q + n1 + nd + n2);
   h->layout = (uint32_t*)(q + n1 + nd + n2 + n3);
+  h->gbounds = (int32_t*)(q + n1 + nd + n2 + n3 + 64);
   h->epoch = 0;
   h->timing = 0;
   h->trec = 0;
@@ -1552,6 +1785,8 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   const bool has_dl = R_d > 0 && in->draft_logits != nullptr;
   if (in->target_stride < V || (has_dl && in->draft_stride < V)) return SPECVERIFY_ERR_INVALID_ARGUMENT;
   const int esize = h->cfg.dtype == SPECVERIFY_F32 ? 4 : 2;
+  if (in->target_stride * esize >= ((int64_t)1 << 31) || (has_dl && in->draft_stride * esize >= ((int64_t)1 << 31)))
+    return SPECVERIFY_ERR_UNSUPPORTED;   // row strides of 2 GB or more
   if (((uintptr_t)in->target_logits % esize) || (has_dl && ((uintptr_t)in->draft_logits % esize)))
     return SPECVERIFY_ERR_UNSUPPORTED;   // logits must be element aligned
   // 16-byte loads need rows and the row length on 16-byte boundaries;
@@ -1560,44 +1795,56 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
                    !(((int64_t)V * esize) & 15) &&
                    (!has_dl || (!((uintptr_t)in->draft_logits & 15) && !((in->draft_stride * esize) & 15)));
 
-  // Persistent grid: per row group, as many waves as the device holds, never
-  // more than the busiest group has items.  Without draft logits: one wave
-  // per item.
+  const bool ragged = in->cu_draft != nullptr;
   const int C = h->chunks;
-  const int64_t items_g = ((R_t + kGroups - 1) / kGroups) * C;
-  const int64_t need = (items_g + kStreamWaves - 1) / kStreamWaves;
-  int64_t wg = has_dl ? h->cap[vec ? 1 : 0] / kGroups : need;
-  if (wg > need) wg = need;
-  if (wg < 1) wg = 1;
-  const int gmax = in->cu_draft == nullptr ? in->gamma : h->cfg.max_gamma;
-  const int fwaves = gmax + 1 < kFinishWaves ? gmax + 1 : kFinishWaves;
-
   if (++h->epoch == 0) h->epoch = 1;   // 0 never tags a slot (workspace is zeroed)
   if (h->epoch >= 0x80000000u) h->epoch = 1;   // the layout flag holds epoch * 2
   Params P;
   P.target = (const char*)in->target_logits;
-  P.draft = (const char*)in->draft_logits;
-  P.tstride_b = in->target_stride * esize;
-  P.dstride_b = in->draft_stride * esize;
+  P.draft = has_dl ? (const char*)in->draft_logits : nullptr;
+  P.tstride_b = (uint32_t)(in->target_stride * esize);
+  P.dstride_b = has_dl ? (uint32_t)(in->draft_stride * esize) : 0u;
   P.tokens = in->draft_tokens;
   P.uniforms = in->uniforms;
   P.temps = in->temperatures;
   P.cu_draft = in->cu_draft;
-  P.rowinfo = in->cu_draft ? h->rowinfo : nullptr;
+  P.rowinfo = ragged ? h->rowinfo : nullptr;
   P.layout = h->layout;
-  P.gamma = in->gamma;
+  P.gbounds = ragged ? h->gbounds : nullptr;
+  // Row groups: contiguous ranges of whole sequences, about R_t / kGroups
+  // target rows each (for a ragged batch the layout kernel splits it).
+  int64_t rows_g;   // most target rows a group can get
+  if (!ragged) {
+    for (int g = 0; g <= kGroups; ++g) {
+      P.gseq[g] = (int32_t)(((int64_t)g * B) / kGroups);
+      P.grow[g] = P.gseq[g] * (in->gamma + 1);
+    }
+    rows_g = ((int64_t)(B + kGroups - 1) / kGroups) * (in->gamma + 1);
+  } else {
+    for (int g = 0; g <= kGroups; ++g) P.gseq[g] = P.grow[g] = 0;
+    rows_g = (R_t + kGroups - 1) / kGroups + h->cfg.max_gamma + 1;
+    if (rows_g > R_t) rows_g = R_t;
+  }
+  // Persistent grid: per row group, as many workgroups as the device holds,
+  // never more than the busiest group has items for.
+  const int64_t need = (rows_g * C + kStreamWaves - 1) / kStreamWaves;
+  int64_t wg = h->cap[vec ? 1 : 0][has_dl ? 1 : 0] / kGroups;
+  if (wg > need) wg = need;
+  if (wg < 1) wg = 1;
+  P.gamma = ragged ? 0 : in->gamma;
   P.B = B;
   P.R_d = (int32_t)R_d;
   P.R_t = (int32_t)R_t;
   P.V = V;
   P.C = C;
   P.Gw = (int32_t)(wg * kStreamWaves);
+  P.Wg = (int32_t)wg;
   P.max_gamma = h->cfg.max_gamma;
   P.epoch = h->epoch;
   P.spin_limit = h->cfg.spin_limit;
   P.token_only = R_d > 0 && !has_dl;
   udiv_consts((uint32_t)C, P.div_c);
-  udiv_consts((uint32_t)(in->cu_draft ? 1 : in->gamma + 1), P.div_g);
+  udiv_consts((uint32_t)(ragged ? 1 : in->gamma + 1), P.div_g);
   P.xch1 = h->xch1;
   P.dummy = h->dummy;
   P.part = h->part;
@@ -1617,10 +1864,11 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   hipEvent_t* ev = nullptr;
   if (h->timing && h->trec < SPECVERIFY_TIMING_RUNS) ev = h->ev + 3 * h->trec++;
   if (ev) e = hipEventRecord(ev[0], stream);
-  if (in->cu_draft) hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, P, h->rowinfo, h->layout);
-  hipLaunchKernelGGL(has_dl ? K.stream : K.stream_t, dim3((uint32_t)(wg * kGroups)), dim3(kStreamThreads), 0, stream, P);
+  if (ragged)
+    hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, P, h->rowinfo, h->gbounds, h->layout);
+  hipLaunchKernelGGL(has_dl ? K.with_draft : K.no_draft, dim3((uint32_t)(wg * kGroups)), dim3(kStreamThreads), 0,
+                     stream, P);
   if (ev && e == hipSuccess) e = hipEventRecord(ev[1], stream);
-  hipLaunchKernelGGL(K.finish, dim3(B), dim3(64 * fwaves), 0, stream, P);
   if (ev && e == hipSuccess) e = hipEventRecord(ev[2], stream);
   const hipError_t e2 = hipGetLastError();
   if (prev != h->cfg.device) (void)hipSetDevice(prev);

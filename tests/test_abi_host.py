@@ -56,3 +56,19 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         binding.load_library(str(tmp_path / "nope.so"))
+
+
+def test_create_without_a_device_fails_cleanly():
+    """On a host with no GPU, create returns SPECVERIFY_ERR_DEVICE, leaves the
+    handle NULL and does not crash (a failure the caller can handle)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present")
+    lib = binding.load_library()
+    h = ctypes.c_void_p(12345)
+    cfg = binding.Config(4, 4, 32000, binding.F32, 0, 0)
+    assert lib.specverify_create(ctypes.byref(cfg), ctypes.byref(h)) == binding.ERR_DEVICE
+    assert not h.value
+    with pytest.raises(binding.SpecVerifyError) as e:
+        binding.SpecVerify(max_batch=4, max_gamma=4, vocab=32000, dtype="f32")
+    assert e.value.status == binding.ERR_DEVICE

@@ -96,11 +96,16 @@ def test_commit_host_errors():
     import torch
     sv = SpecVerify(max_batch=4, max_gamma=2, vocab=1000, dtype="bf16")
     z = torch.zeros(4, dtype=torch.int32, device="cuda:0")
-    t = torch.zeros((4, 8), dtype=torch.int32, device="cuda:0")
+    z5 = torch.zeros(5, dtype=torch.int32, device="cuda:0")
+    o = torch.zeros(40, dtype=torch.int32, device="cuda:0")
+    t = torch.zeros((5, 8), dtype=torch.int32, device="cuda:0")
+    # the library's own limits, with tensors the binding's checks accept
     with pytest.raises(SpecVerifyError):
-        sv.commit(torch.zeros(5, dtype=torch.int32, device="cuda:0"), z, t, z, gamma=1)   # B > max_batch
+        sv.commit(z5, o, t, z5, gamma=1)                      # B > max_batch
     with pytest.raises(SpecVerifyError):
-        sv.commit(z, z, t, z, gamma=3)                                                   # gamma > max_gamma
+        sv.commit(z, o, t, z, gamma=3)                        # gamma > max_gamma
+    with pytest.raises(ValueError):                           # the binding: too few out_tokens
+        sv.commit(z, z, t, z, gamma=1)
 
 
 @pytest.mark.parametrize("tok", [False, True])

@@ -254,13 +254,13 @@ def test_invalid_data_flagged_per_sequence(case):
 
 
 def test_repeated_runs_bitwise_identical():
-    """Fixed reduction order: 20 launches on the same buffers give the same bits."""
+    """Fixed reduction order: 100 launches on the same buffers give the same bits."""
     import torch
     inp = make_inputs("b64_g4_v128256_bf16", seed=3, batch=16)
     sv = _handle(inp)
     dev = to_device(inp)
     ref = None
-    for k in range(20):
+    for k in range(100):
         out = alloc_outputs(inp)
         gpu_run(sv, dev, out, inp)
         got = fetch(out)
@@ -312,13 +312,19 @@ def test_host_validation_errors():
     sv = SpecVerify(max_batch=2, max_gamma=4, vocab=32000, dtype="f32")
     dev = to_device(inp)
     out = alloc_outputs(inp)
-    with pytest.raises(SpecVerifyError) as e:      # gamma beyond the handle's limit
+    lib = __import__("rejection_sampling_verifier_specverify_amd.binding", fromlist=["x"])
+    with pytest.raises(ValueError):                # the binding: 5 drafts per sequence need 5 tokens
         sv.run(dev["target"], dev["draft"], dev["draft_tokens"], dev["uniforms"], dev["temperatures"],
                gamma=5, **out)
+    with pytest.raises(SpecVerifyError) as e:      # the library: gamma beyond the handle's limit
+        inp_c = lib.Inputs(1, 5, None, 5, dev["target"].data_ptr(), 32000, dev["draft"].data_ptr(), 32000,
+                           dev["draft_tokens"].data_ptr(), dev["uniforms"].data_ptr(),
+                           dev["temperatures"].data_ptr())
+        out_c = lib.Outputs(out["accepted_len"].data_ptr(), out["out_tokens"].data_ptr(), None, None, None, None)
+        lib.specverify_run(sv.handle, inp_c, out_c, torch.cuda.current_stream().cuda_stream)
     assert e.value.status == ERR_INVALID_ARGUMENT
     with pytest.raises(SpecVerifyError) as e:      # logits not aligned to their element size
         raw = torch.zeros(5 * 32000 * 4 + 4, dtype=torch.uint8, device="cuda:0")
-        lib = __import__("rejection_sampling_verifier_specverify_amd.binding", fromlist=["x"])
         inp_c = lib.Inputs(1, 4, None, 4, raw.data_ptr() + 1, 32000, dev["draft"].data_ptr(), 32000,
                            dev["draft_tokens"].data_ptr(), dev["uniforms"].data_ptr(),
                            dev["temperatures"].data_ptr())
