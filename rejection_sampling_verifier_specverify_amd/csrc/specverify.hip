@@ -1104,10 +1104,10 @@ struct SampleJob {
 // and, for the wave's first row that needs the final sample (a rejected
 // draft, or the bonus row), the owner chunk, whose logits are loaded into R.
 // Returns the row result (accepted rows carry their draft token).
-template <int DT, bool VEC, int NPER>
+template <int DT, bool VEC, bool D, int NPER>
 __device__ __forceinline__ uint32_t accept_sampled(const Params& P, int j, int r, int rd, bool pair, bool dp, float T,
-                                                   float ui, float ug, int lane, const RowIn<NPER>& in, SampleJob& job,
-                                                   u32x4 (&R)[2][kU]) {
+                                                   float ui, float ug, int lane, const RowIn<NPER>& in, float lx,
+                                                   float dx, SampleJob& job, u32x4 (&R)[2][kU]) {
   using F = Fmt<DT>;
   const int C = P.C;
   const float s = kLog2e / T;
@@ -1123,11 +1123,6 @@ __device__ __forceinline__ uint32_t accept_sampled(const Params& P, int j, int r
     const bool inr = dp && lane + 64 * jj < C;
     W[jj] = inr ? in.pt[jj].y : 0.0f;
     Bp[jj] = inr ? in.pt[jj].z : 0.0f;
-  }
-  float lx = 0.0f, dx = 0.0f;
-  if (dp && x_ok) {   // token-only rows read e_t at x from the slots instead
-    lx = load_logit<DT>(P.target, r, P.tstride_b, x);
-    dx = load_logit<DT>(P.draft, rd, P.dstride_b, x);
   }
   float Mt, St, Md = ninf, Sd = 0.0f;
   merge_row(q, C, 0, s, lane, Mt, St);
@@ -1251,7 +1246,7 @@ __device__ __forceinline__ uint32_t accept_sampled(const Params& P, int j, int r
   // re-read the owner chunk now: its loads land while the other rows resolve
   const int nb = P.V * F::ESIZE;
   issue_row<DT, VEC>(chunk_rsrc(P.target, r, P.tstride_b, cs, nb, true), lane, R[0]);
-  issue_row<DT, VEC>(chunk_rsrc(P.draft, rd, P.dstride_b, cs, nb, resid && dp), lane, R[1]);
+  if (D) issue_row<DT, VEC>(chunk_rsrc(P.draft, rd, P.dstride_b, cs, nb, resid && dp), lane, R[1]);
   return row_payload(0, false, 0);
 }
 
@@ -1262,25 +1257,25 @@ __device__ __forceinline__ uint32_t accept_sampled(const Params& P, int j, int r
 // one branch per row around straight-line code), a wave scan of the lane
 // sums and the first position whose running sum exceeds tau.  Rounds go in
 // order and stop at the first with a hit.  Returns the token, or -1.
-template <int DT>
+template <int DT, bool D>
 __device__ __forceinline__ int sample_scan(const Params& P, const SampleJob& job, float s, int lane,
                                            u32x4 (&R)[2][kU]) {
   using F = Fmt<DT>;
   const int cs = job.cs;
   if ((cs + 1) * F::CH > P.V) {   // tokens >= V: weight 0
     mask_raw<DT>(R[0], cs, P.V, lane);
-    mask_raw<DT>(R[1], cs, P.V, lane);
+    if (D) mask_raw<DT>(R[1], cs, P.V, lane);
   }
   int first = 0x7FFFFFFF, lastpos = -1;
   float rbase = 0.0f;
 #pragma unroll 1
   for (int u = 0; u < kU; ++u) {
     // the round's two vectors, picked by selects (u is wave-uniform)
-    u32x4 vt = R[0][0], vd = R[1][0];
+    u32x4 vt = R[0][0], vd = R[D ? 1 : 0][0];
 #pragma unroll
     for (int i = 1; i < kU; ++i) {
       vt = i == u ? R[0][i] : vt;
-      vd = i == u ? R[1][i] : vd;
+      if (D) vd = i == u ? R[1][i] : vd;
     }
     float w[F::EPV];
     if (job.tk && job.resid) {
@@ -1289,7 +1284,7 @@ __device__ __forceinline__ int sample_scan(const Params& P, const SampleJob& job
         const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vt, e), s, job.ct));
         w[e] = token_of<DT>(cs, u * F::EPV + e, lane) == job.x ? 0.0f : et;
       }
-    } else if (job.resid) {
+    } else if (D && job.resid) {
 #pragma unroll
       for (int e = 0; e < F::EPV; ++e)
         w[e] = resid_w(__builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vt, e), s, job.ct)),
@@ -1385,6 +1380,13 @@ __device__ __forceinline__ uint32_t resolve_row(const Params& P, int j, int r, i
   chunk_offsets(P.C, lane, kPart * (int)sizeof(float), poff);
   RowIn<NPER> in;
   in.x = pair ? ld_const(P.tokens, rd) : 0;
+  // the logits at x go out before the polls, so that they have landed when
+  // the row's statistics have (token-only rows read e_t at x from the slots)
+  float lx = 0.0f, dx = 0.0f;
+  if (sampled && dp && in.x >= 0 && in.x < P.V) {
+    lx = load_logit<DT>(P.target, r, P.tstride_b, in.x);
+    dx = load_logit<DT>(P.draft, rd, P.dstride_b, in.x);
+  }
   for (int k = 0;; ++k) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the loads below are read again on every turn
     slots_issue(P, r, true, soff, in.q);
@@ -1408,7 +1410,7 @@ __device__ __forceinline__ uint32_t resolve_row(const Params& P, int j, int r, i
       __builtin_amdgcn_s_sleep(2);
     }
   }
-  if (sampled) return accept_sampled<DT, VEC, NPER>(P, j, r, rd, pair, dp, T, ui, ug, lane, in, job, R);
+  if (sampled) return accept_sampled<DT, VEC, D, NPER>(P, j, r, rd, pair, dp, T, ui, ug, lane, in, lx, dx, job, R);
   return finish_greedy<NPER>(P, rd, pair, dp, lane, in);
 }
 
@@ -1457,7 +1459,7 @@ __device__ __forceinline__ void resolve_sequence(const Params& P, int b, int lan
     if (st == 0) {
       if (sampled) {
         // job.row == n here: every row of this wave before n was accepted
-        tn = job.row == n ? sample_scan<DT>(P, job, kLog2e / T, lane, R) : -1;
+        tn = job.row == n ? sample_scan<DT, D>(P, job, kLog2e / T, lane, R) : -1;
         if (tn < 0) st = 2;   // unreachable
       } else {
         tn = (int)(shres[n] & kTokMask);   // greedy: the argmax
