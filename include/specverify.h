@@ -205,6 +205,21 @@ specverify_status specverify_set_timing(specverify_handle h, int32_t enable);
 specverify_status specverify_timing_totals(specverify_handle h, int32_t* runs, float* stream_ms,
                                            float* finish_ms);
 
+/* Measurement probe (for benchmarks, not part of the method): one launch on
+ * hip_stream that reads every byte of the ranges [a, a + a_bytes) and
+ * [b, b + b_bytes) of device memory once, in 4 KB chunks with 16-byte
+ * nontemporal loads spread over the whole device (the verification kernel's
+ * access pattern), and does nothing else; it XOR-folds the words per wave
+ * and writes a fold to *sink (one device uint32) only when it equals the
+ * constant 0x9E3779B9, so *sink is normally left as it was; the condition
+ * keeps every load.  Its bandwidth is the device's
+ * practical streaming-read ceiling for the bytes a run reads (pass the
+ * target and draft logits).  Pointers 16-byte aligned, sizes multiples of
+ * 16, else INVALID_ARGUMENT; DEVICE if the launch fails.  Uses the current
+ * HIP device. */
+specverify_status specverify_probe_read(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes,
+                                        uint32_t* sink, void* hip_stream);
+
 /* Number of V-chunks (4 KB of a row: 2048 bf16 or 1024 f32 logits) a row
  * is split into for this handle, and the workspace size in bytes; for tools
  * and tests. */

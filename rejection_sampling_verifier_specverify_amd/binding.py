@@ -24,7 +24,8 @@ CHUNK = {"bf16": 2048, "f32": 1024}   # logits per V-chunk (4 KB of a row: one w
 MAX_CHUNKS = {"bf16": 128, "f32": 256}
 EXPORTED = ("specverify_create", "specverify_run", "specverify_destroy",
             "specverify_set_timing", "specverify_timing_totals",
-            "specverify_chunks_per_row", "specverify_workspace_bytes", "specverify_commit")
+            "specverify_chunks_per_row", "specverify_workspace_bytes", "specverify_commit",
+            "specverify_probe_read")
 
 
 class Config(ctypes.Structure):
@@ -102,6 +103,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.specverify_timing_totals.restype = ctypes.c_int
     lib.specverify_commit.argtypes = [ctypes.c_void_p, ctypes.POINTER(CommitArgs), ctypes.c_void_p]
     lib.specverify_commit.restype = ctypes.c_int
+    lib.specverify_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    lib.specverify_probe_read.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -125,6 +129,16 @@ def specverify_commit(h: ctypes.c_void_p, args: CommitArgs, stream: int) -> None
     st = load_library().specverify_commit(h, ctypes.byref(args), ctypes.c_void_p(stream))
     if st != OK:
         raise SpecVerifyError("specverify_commit", st)
+
+
+def specverify_probe_read(a, b, sink, stream: int) -> None:
+    """The streaming-read probe over two device tensors (see the header)."""
+    st = load_library().specverify_probe_read(
+        ctypes.c_void_p(a.data_ptr()), a.numel() * a.element_size(),
+        ctypes.c_void_p(b.data_ptr() if b is not None else 0), 0 if b is None else b.numel() * b.element_size(),
+        ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream))
+    if st != OK:
+        raise SpecVerifyError("specverify_probe_read", st)
 
 
 def specverify_destroy(h: ctypes.c_void_p) -> None:

@@ -1622,6 +1622,50 @@ __global__ __launch_bounds__(64 * kCommitWaves) void commit_kernel(CommitParams 
   }
 }
 
+// ================================================================== read probe (measurement)
+
+// A plain streaming read of two byte ranges, and nothing else: the practical
+// read bandwidth of the device for the bytes a run streams.  The ranges are
+// cut into 4 KB chunks, read the way the verification kernel reads an item
+// (one wave per chunk, four 16-byte nontemporal loads per lane through a
+// buffer over the chunk, two chunks in flight per wave).  The words are
+// XOR-folded per wave; the fold is stored to *sink only when it equals
+// kProbeKey, a condition the compiler cannot decide, so no load is dropped.
+constexpr int kProbeThreads = 256;
+constexpr uint32_t kProbeKey = 0x9E3779B9u;
+__device__ __forceinline__ Rsrc probe_chunk(const char* a, int64_t na, const char* b, int64_t nb, int64_t ca,
+                                            int64_t k) {
+  const bool in_a = k < ca;
+  const int64_t off = (in_a ? k : k - ca) * kRowBytes;
+  const int64_t n = in_a ? na - off : nb - off;   // <= 0 past the end: a zero-sized buffer
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((in_a ? a : b) + (n > 0 ? off : 0)), (short)0,
+                                           n <= 0 ? 0 : (n > kRowBytes ? kRowBytes : (int)n), kRsrcWord3);
+}
+__global__ __launch_bounds__(kProbeThreads) void probe_kernel(const char* a, int64_t na, const char* b, int64_t nb,
+                                                              uint32_t* sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (kProbeThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (kProbeThreads / 64);
+  const int64_t ca = (na + kRowBytes - 1) / kRowBytes, nch = ca + (nb + kRowBytes - 1) / kRowBytes;
+  uint32_t acc = 0;
+  for (int64_t k0 = wave; k0 < nch; k0 += 2 * nwaves) {
+    const Rsrc r0 = probe_chunk(a, na, b, nb, ca, k0);
+    const Rsrc r1 = probe_chunk(a, na, b, nb, ca, k0 + nwaves);
+    u32x4 w0[kU], w1[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) w0[u] = __builtin_amdgcn_raw_buffer_load_b128(r0, lane * 16 + u * 1024, 0, kNT);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) w1[u] = __builtin_amdgcn_raw_buffer_load_b128(r1, lane * 16 + u * 1024, 0, kNT);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) acc ^= w0[u][0] ^ w0[u][1] ^ w0[u][2] ^ w0[u][3] ^ w1[u][0] ^ w1[u][1] ^ w1[u][2] ^ w1[u][3];
+  }
+  acc = (uint32_t)wave_max_i((int)acc) ^ (uint32_t)wave_min_i((int)acc);
+  // a store that depends on every word keeps every load; it is taken only
+  // for one fold value in 2^32 (one store per wave would serialise on the
+  // one address)
+  if (lane == 0 && acc == kProbeKey) sink[0] = acc;
+}
+
 // ================================================================== launch table
 
 typedef void (*KernelFn)(Params);
@@ -1977,6 +2021,25 @@ specverify_status specverify_timing_totals(specverify_handle h, int32_t* runs, f
   *finish_ms = (float)f;
   h->trec = 0;
   return SPECVERIFY_OK;
+}
+
+specverify_status specverify_probe_read(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes,
+                                        uint32_t* sink, void* hip_stream) {
+  if (!sink || a_bytes < 0 || b_bytes < 0 || (a_bytes > 0 && !a) || (b_bytes > 0 && !b) || (a_bytes % 16) ||
+      (b_bytes % 16) || ((uintptr_t)a % 16) || ((uintptr_t)b % 16))
+    return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return SPECVERIFY_ERR_DEVICE;
+  const int64_t chunks = (a_bytes + kRowBytes - 1) / kRowBytes + (b_bytes + kRowBytes - 1) / kRowBytes;
+  int64_t grid = (int64_t)cus * 8;   // eight workgroups of four waves per CU
+  const int64_t need = (chunks + 2 * (kProbeThreads / 64) - 1) / (2 * (kProbeThreads / 64));
+  if (grid > need) grid = need;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(probe_kernel, dim3((uint32_t)grid), dim3(kProbeThreads), 0, (hipStream_t)hip_stream,
+                     (const char*)a, a_bytes, (const char*)b, b_bytes, sink);
+  return hipGetLastError() == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_ERR_DEVICE;
 }
 
 int32_t specverify_chunks_per_row(specverify_handle h) { return h ? h->chunks : 0; }
