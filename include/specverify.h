@@ -77,7 +77,8 @@ typedef enum {
   SPECVERIFY_ERR_INVALID_ARGUMENT = 1, /* bad pointer / size / config     */
   SPECVERIFY_ERR_UNSUPPORTED = 2,      /* unaligned logits, V too big     */
   SPECVERIFY_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed     */
-  SPECVERIFY_ERR_DEVICE = 4            /* HIP runtime / launch failure    */
+  SPECVERIFY_ERR_DEVICE = 4,           /* HIP runtime / launch failure    */
+  SPECVERIFY_ERR_TOO_LARGE = 5         /* run_static: beyond its scratch  */
 } specverify_status;
 
 typedef enum { SPECVERIFY_F32 = 0, SPECVERIFY_BF16 = 1 } specverify_dtype;
@@ -146,6 +147,32 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
  * size; DEVICE if the launch fails. */
 specverify_status specverify_run(specverify_handle h, const specverify_inputs* in,
                                  const specverify_outputs* out, void* hip_stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * run as specverify_run, with the same kernels, results, arguments and
+ * errors, but without a handle.  cfg is read as by specverify_create (its
+ * limits bound this call's batch); the workspace is a 16 MiB array of the
+ * library in device memory, one per device, that the device holds until the
+ * process ends.  The call allocates nothing: the first call on a device
+ * looks up that device's array (hipGetSymbolAddress) and clears it with a
+ * kernel on hip_stream; later calls launch only the run.  A run needs
+ * 48 * R_t * C bytes (C = ceil(V / 2048) for bf16, ceil(V / 1024) for f32)
+ * plus 64 bytes per wave of its grid (at most the device's resident waves,
+ * 0.5 MiB on an MI355X) and a few KB, each region rounded up to 256 bytes;
+ * a run that needs more than 16 MiB returns TOO_LARGE before any launch
+ * (B = 64, gamma = 4, V = 128256 bf16 needs 1.1 MiB; B = 512 with 2601
+ * target rows at V = 152064, 9.1 MiB).  UNSUPPORTED also for a device
+ * ordinal of 64 or more.
+ * Every call on a device shares its array and leaves its contents there;
+ * what a run reads from it carries the run's epoch, a per-device counter
+ * kept on the host, so stale contents are never taken for new ones.  Calls
+ * on one device must not overlap: put them on one stream or order them
+ * (overlapping calls race on the array).  A captured graph keeps the epoch
+ * it was captured with, so replaying it more than once is not supported.
+ * Thread-safe on the host. */
+specverify_status specverify_run_static(const specverify_config* cfg, const specverify_inputs* in,
+                                        const specverify_outputs* out, void* hip_stream);
 
 /* On-device commit of a verification step (Perplexity "Accelerating Sonar
  * through speculation", section "단일 토큰에 대한 MTP 스케줄링": after the drafts

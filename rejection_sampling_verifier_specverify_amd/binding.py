@@ -17,15 +17,16 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # SPECVERIFY_LIB selects another build of the library (same ABI)
 LIB_PATH = os.environ.get("SPECVERIFY_LIB", os.path.join(PKG, "libspecverify.so"))
 
-OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_OUT_OF_MEMORY, ERR_DEVICE = range(5)
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_OUT_OF_MEMORY, ERR_DEVICE, ERR_TOO_LARGE = range(6)
 F32, BF16 = 0, 1
-STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "DEVICE"}
+STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "DEVICE",
+                5: "TOO_LARGE"}
 CHUNK = {"bf16": 2048, "f32": 1024}   # logits per V-chunk (4 KB of a row: one wave's item)
 MAX_CHUNKS = {"bf16": 128, "f32": 256}
 EXPORTED = ("specverify_create", "specverify_run", "specverify_destroy",
             "specverify_set_timing", "specverify_timing_totals",
             "specverify_chunks_per_row", "specverify_workspace_bytes", "specverify_commit",
-            "specverify_probe_read")
+            "specverify_probe_read", "specverify_run_static")
 
 
 class Config(ctypes.Structure):
@@ -89,6 +90,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.specverify_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(Inputs), ctypes.POINTER(Outputs),
                                    ctypes.c_void_p]
     lib.specverify_run.restype = ctypes.c_int
+    lib.specverify_run_static.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Inputs), ctypes.POINTER(Outputs),
+                                          ctypes.c_void_p]
+    lib.specverify_run_static.restype = ctypes.c_int
     lib.specverify_destroy.argtypes = [ctypes.c_void_p]
     lib.specverify_destroy.restype = ctypes.c_int
     lib.specverify_chunks_per_row.argtypes = [ctypes.c_void_p]
@@ -123,6 +127,13 @@ def specverify_run(h: ctypes.c_void_p, inputs: Inputs, outputs: Outputs, stream:
                                        ctypes.c_void_p(stream))
     if st != OK:
         raise SpecVerifyError("specverify_run", st)
+
+
+def specverify_run_static(cfg: Config, inputs: Inputs, outputs: Outputs, stream: int) -> None:
+    st = load_library().specverify_run_static(ctypes.byref(cfg), ctypes.byref(inputs), ctypes.byref(outputs),
+                                              ctypes.c_void_p(stream))
+    if st != OK:
+        raise SpecVerifyError("specverify_run_static", st)
 
 
 def specverify_commit(h: ctypes.c_void_p, args: CommitArgs, stream: int) -> None:
@@ -254,6 +265,44 @@ def check_commit_args(*, device, accepted_len, out_tokens, seq_tokens, seq_lens,
     return B, R_t
 
 
+def _marshal_run(cfg, target, draft, draft_tokens, uniforms, temperatures, accepted_len, out_tokens, gamma,
+                 cu_draft, num_draft_rows, p_draft, q_draft, beta, resid_mass, stream):
+    """Check the tensors of a run against cfg (.dtype, .vocab, .device) and
+    fill the C structs; returns (Inputs, Outputs, stream handle)."""
+    import torch
+    want = torch.float32 if cfg.dtype == F32 else torch.bfloat16
+    batch, R_d, _ = check_run_args(
+        vocab=cfg.vocab, logits_dtype=want, device=torch.device("cuda", cfg.device), target=target,
+        draft=draft, draft_tokens=draft_tokens, uniforms=uniforms, temperatures=temperatures,
+        accepted_len=accepted_len, out_tokens=out_tokens, gamma=gamma, cu_draft=cu_draft,
+        num_draft_rows=num_draft_rows,
+        diagnostics=(("p_draft", p_draft), ("q_draft", q_draft), ("beta", beta), ("resid_mass", resid_mass)))
+    inp = Inputs()
+    inp.batch = batch
+    if cu_draft is None:
+        inp.gamma = int(gamma)
+        inp.cu_draft = None
+        inp.num_draft_rows = R_d
+    else:
+        inp.gamma = 0
+        inp.cu_draft = _ptr(cu_draft)
+        inp.num_draft_rows = R_d
+    inp.target_logits = _ptr(target)
+    inp.target_stride = int(target.stride(0))
+    # draft None with drafted tokens: token-only drafts (q_i = delta_{x_i})
+    has_draft = draft is not None and draft.numel() > 0
+    inp.draft_logits = _ptr(draft) if has_draft else None
+    inp.draft_stride = int(draft.stride(0)) if has_draft else int(cfg.vocab)
+    has_tokens = draft_tokens is not None and draft_tokens.numel() > 0
+    inp.draft_tokens = _ptr(draft_tokens) if has_tokens else None
+    inp.uniforms = _ptr(uniforms)
+    inp.temperatures = _ptr(temperatures)
+    out = Outputs(_ptr(accepted_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),
+                  _ptr(beta), _ptr(resid_mass))
+    s = stream if stream is not None else torch.cuda.current_stream(cfg.device).cuda_stream
+    return inp, out, int(s)
+
+
 class SpecVerify:
     """A handle bound to one device, vocabulary and logits dtype.
 
@@ -302,38 +351,10 @@ class SpecVerify:
     def run(self, target, draft, draft_tokens, uniforms, temperatures, accepted_len, out_tokens, *,
             gamma: Optional[int] = None, cu_draft=None, num_draft_rows: Optional[int] = None,
             p_draft=None, q_draft=None, beta=None, resid_mass=None, stream=None) -> None:
-        import torch
-        want = torch.float32 if self.dtype == F32 else torch.bfloat16
-        batch, R_d, _ = check_run_args(
-            vocab=self.vocab, logits_dtype=want, device=torch.device("cuda", self.device), target=target,
-            draft=draft, draft_tokens=draft_tokens, uniforms=uniforms, temperatures=temperatures,
-            accepted_len=accepted_len, out_tokens=out_tokens, gamma=gamma, cu_draft=cu_draft,
-            num_draft_rows=num_draft_rows,
-            diagnostics=(("p_draft", p_draft), ("q_draft", q_draft), ("beta", beta), ("resid_mass", resid_mass)))
-        inp = Inputs()
-        inp.batch = batch
-        if cu_draft is None:
-            inp.gamma = int(gamma)
-            inp.cu_draft = None
-            inp.num_draft_rows = R_d
-        else:
-            inp.gamma = 0
-            inp.cu_draft = _ptr(cu_draft)
-            inp.num_draft_rows = R_d
-        inp.target_logits = _ptr(target)
-        inp.target_stride = int(target.stride(0))
-        # draft None with drafted tokens: token-only drafts (q_i = delta_{x_i})
-        has_draft = draft is not None and draft.numel() > 0
-        inp.draft_logits = _ptr(draft) if has_draft else None
-        inp.draft_stride = int(draft.stride(0)) if has_draft else int(self.vocab)
-        has_tokens = draft_tokens is not None and draft_tokens.numel() > 0
-        inp.draft_tokens = _ptr(draft_tokens) if has_tokens else None
-        inp.uniforms = _ptr(uniforms)
-        inp.temperatures = _ptr(temperatures)
-        out = Outputs(_ptr(accepted_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),
-                      _ptr(beta), _ptr(resid_mass))
-        s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
-        specverify_run(self.handle, inp, out, int(s))
+        inp, out, s = _marshal_run(self, target, draft, draft_tokens, uniforms, temperatures, accepted_len,
+                                   out_tokens, gamma, cu_draft, num_draft_rows, p_draft, q_draft, beta,
+                                   resid_mass, stream)
+        specverify_run(self.handle, inp, out, s)
 
     def commit(self, accepted_len, out_tokens, seq_tokens, seq_lens, *, gamma: Optional[int] = None,
                cu_draft=None, num_draft_rows: Optional[int] = None, appended=None, next_token=None,
@@ -366,3 +387,27 @@ class SpecVerify:
         a.next_token = _ptr(next_token)
         s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
         specverify_commit(self.handle, a, int(s))
+
+
+class SpecVerifyStatic:
+    """Runs without a handle or any device allocation (specverify_run_static):
+    the same ``run`` as SpecVerify, on the library's per-device static
+    scratch.  Calls on one device must be ordered (one stream)."""
+
+    def __init__(self, max_batch: int, max_gamma: int, vocab: int, dtype: str = "bf16",
+                 device: int = 0, spin_limit: int = 0):
+        self.dtype = {"f32": F32, "bf16": BF16}[dtype]
+        self.vocab = vocab
+        self.device = device
+        self.cfg = Config(max_batch, max_gamma, vocab, self.dtype, device, spin_limit)
+
+    def run(self, target, draft, draft_tokens, uniforms, temperatures, accepted_len, out_tokens, *,
+            gamma: Optional[int] = None, cu_draft=None, num_draft_rows: Optional[int] = None,
+            p_draft=None, q_draft=None, beta=None, resid_mass=None, stream=None) -> None:
+        inp, out, s = _marshal_run(self, target, draft, draft_tokens, uniforms, temperatures, accepted_len,
+                                   out_tokens, gamma, cu_draft, num_draft_rows, p_draft, q_draft, beta,
+                                   resid_mass, stream)
+        specverify_run_static(self.cfg, inp, out, s)
+
+    def close(self) -> None:
+        pass

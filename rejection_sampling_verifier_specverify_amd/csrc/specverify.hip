@@ -69,6 +69,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <new>
 
 #include "specverify.h"
@@ -85,6 +86,7 @@ constexpr int kGroups = 8;                     // row groups = XCDs of an MI355X
 constexpr int kX1 = 4;                         // exchange slots per (row, chunk)
 constexpr int kPart = 4;                       // floats of partials per (row, chunk)
 constexpr int kMaxGamma = 255;                 // rows per sequence <= 256
+constexpr size_t kScratchBytes = (size_t)16 << 20;   // the static scratch of allocation-free runs, per device
 constexpr int kLayoutThreads = 1024;
 constexpr int kDefaultSpin = 64;               // polls (~1 us each) before a wave computes missing chunks itself
 constexpr int kMaxSpin = 1 << 20;
@@ -1698,6 +1700,275 @@ void udiv_consts(uint32_t d, uint32_t (&k)[3]) {
   k[2] = l > 1 ? l - 1 : 0;
 }
 
+// ================================================================== host: checks and launch
+
+// The limits of a configuration (see specverify_config); C = chunks per row.
+specverify_status check_config(const specverify_config* cfg, int& C) {
+  if (!cfg) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  if (cfg->max_batch < 1 || cfg->max_gamma < 0 || cfg->max_gamma > kMaxGamma || cfg->vocab < 1 ||
+      cfg->spin_limit < 0 || (cfg->dtype != SPECVERIFY_F32 && cfg->dtype != SPECVERIFY_BF16))
+    return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  const int64_t rows = (int64_t)cfg->max_batch * ((int64_t)cfg->max_gamma + 1);
+  if (rows > (int64_t)1 << 24) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  C = chunks_for(cfg->vocab, cfg->dtype);
+  if (C > max_chunks(cfg->dtype)) return SPECVERIFY_ERR_UNSUPPORTED;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev)
+    return SPECVERIFY_ERR_DEVICE;
+  return SPECVERIFY_OK;
+}
+int spin_of(const specverify_config& cfg) {
+  return cfg.spin_limit == 0 ? kDefaultSpin : cfg.spin_limit > kMaxSpin ? kMaxSpin : cfg.spin_limit;
+}
+
+// Residency of the persistent grids of a (dtype, nper) build on the current
+// device: workgroups per CU times CUs, [vector loads][draft logits].  With
+// draft logits a row group needs at least C waves, so that the chunks of a
+// row fall into one round or two consecutive ones and their waves meet in
+// time.  A kernel that spilled to scratch would make the runtime allocate
+// scratch at its first launch and spill in its inner loop: such a build is
+// refused rather than run (hipErrorInvalidConfiguration).
+hipError_t kernel_caps(int dtype, int nper, int C, int device, int (&cap)[2][2], int& capmax) {
+  int cus = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  capmax = 0;
+  for (int v = 0; v < 4 && e == hipSuccess; ++v) {
+    const bool vec = (v & 1) == 1, dl = v < 2;
+    const Kernels K = kernels_for(dtype, vec, nper);
+    const void* fn = (const void*)(dl ? K.with_draft : K.no_draft);
+    hipFuncAttributes fa;
+    e = hipFuncGetAttributes(&fa, fn);
+    if (e == hipSuccess && fa.localSizeBytes > 0) e = hipErrorInvalidConfiguration;
+    int per_cu = 0;
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStreamThreads, 0);
+    cap[vec][dl] = cus * per_cu;
+    if (cap[vec][dl] > capmax) capmax = cap[vec][dl];
+    if (e == hipSuccess && (per_cu < 1 || (dl && (cap[vec][dl] / kGroups) * kStreamWaves < C)))
+      e = hipErrorInvalidConfiguration;
+  }
+  return e;
+}
+
+// One run's launch: everything of Params but the workspace and the epoch.
+struct Plan {
+  Params P;
+  Kernels K;
+  bool ragged, has_dl;
+  int64_t wg;     // workgroups per row group
+  int64_t R_t;    // 0: an empty batch, nothing to launch
+};
+
+// The workspace of one launch (device memory).
+struct Workspace {
+  uint64_t* xch1;
+  uint64_t* dummy;
+  float* part;
+  int4* rowinfo;
+  uint32_t* layout;
+  int32_t* gbounds;
+};
+
+// Check one run's arguments against a configuration (C chunks per row, at
+// most max_rows target rows, resident workgroups cap) and plan its launch.
+specverify_status plan_run(const specverify_config& cfg, int C, int nper, int64_t max_rows, const int (&cap)[2][2],
+                           const specverify_inputs* in, const specverify_outputs* out, Plan& pl) {
+  pl.R_t = 0;
+  if (!in || !out) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  const int B = in->batch;
+  if (B < 0 || B > cfg.max_batch) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  if (B == 0) return SPECVERIFY_OK;
+  int64_t R_d;
+  if (in->cu_draft == nullptr) {
+    if (in->gamma < 0 || in->gamma > cfg.max_gamma) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+    R_d = (int64_t)B * in->gamma;
+  } else {
+    if (in->num_draft_rows < 0) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+    R_d = in->num_draft_rows;
+  }
+  const int64_t R_t = R_d + B;
+  if (R_t > max_rows) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  const int V = cfg.vocab;
+  if (!in->target_logits || !in->uniforms || !in->temperatures || !out->accepted_len ||
+      !out->out_tokens)
+    return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  if (R_d > 0 && !in->draft_tokens) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  // drafts without logits are token-only drafts: q_i = delta_{x_i}
+  const bool has_dl = R_d > 0 && in->draft_logits != nullptr;
+  if (in->target_stride < V || (has_dl && in->draft_stride < V)) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  const int esize = cfg.dtype == SPECVERIFY_F32 ? 4 : 2;
+  if (in->target_stride * esize >= ((int64_t)1 << 31) || (has_dl && in->draft_stride * esize >= ((int64_t)1 << 31)))
+    return SPECVERIFY_ERR_UNSUPPORTED;   // row strides of 2 GB or more
+  if (((uintptr_t)in->target_logits % esize) || (has_dl && ((uintptr_t)in->draft_logits % esize)))
+    return SPECVERIFY_ERR_UNSUPPORTED;   // logits must be element aligned
+  // 16-byte loads need rows and the row length on 16-byte boundaries;
+  // otherwise the kernels read element by element.
+  const bool vec = !((uintptr_t)in->target_logits & 15) && !((in->target_stride * esize) & 15) &&
+                   !(((int64_t)V * esize) & 15) &&
+                   (!has_dl || (!((uintptr_t)in->draft_logits & 15) && !((in->draft_stride * esize) & 15)));
+
+  const bool ragged = in->cu_draft != nullptr;
+  Params& P = pl.P;
+  P.target = (const char*)in->target_logits;
+  P.draft = has_dl ? (const char*)in->draft_logits : nullptr;
+  P.tstride_b = (uint32_t)(in->target_stride * esize);
+  P.dstride_b = has_dl ? (uint32_t)(in->draft_stride * esize) : 0u;
+  P.tokens = in->draft_tokens;
+  P.uniforms = in->uniforms;
+  P.temps = in->temperatures;
+  P.cu_draft = in->cu_draft;
+  // Row groups: contiguous ranges of whole sequences, about R_t / kGroups
+  // target rows each (for a ragged batch the layout kernel splits it).
+  int64_t rows_g;   // most target rows a group can get
+  if (!ragged) {
+    for (int g = 0; g <= kGroups; ++g) {
+      P.gseq[g] = (int32_t)(((int64_t)g * B) / kGroups);
+      P.grow[g] = P.gseq[g] * (in->gamma + 1);
+    }
+    rows_g = ((int64_t)(B + kGroups - 1) / kGroups) * (in->gamma + 1);
+  } else {
+    for (int g = 0; g <= kGroups; ++g) P.gseq[g] = P.grow[g] = 0;
+    rows_g = (R_t + kGroups - 1) / kGroups + cfg.max_gamma + 1;
+    if (rows_g > R_t) rows_g = R_t;
+  }
+  // Persistent grid: per row group, as many workgroups as the device holds,
+  // never more than the busiest group has items for.
+  const int64_t need = (rows_g * C + kStreamWaves - 1) / kStreamWaves;
+  int64_t wg = cap[vec ? 1 : 0][has_dl ? 1 : 0] / kGroups;
+  if (wg > need) wg = need;
+  if (wg < 1) wg = 1;
+  P.gamma = ragged ? 0 : in->gamma;
+  P.B = B;
+  P.R_d = (int32_t)R_d;
+  P.R_t = (int32_t)R_t;
+  P.V = V;
+  P.C = C;
+  P.Gw = (int32_t)(wg * kStreamWaves);
+  P.Wg = (int32_t)wg;
+  P.max_gamma = cfg.max_gamma;
+  P.spin_limit = spin_of(cfg);
+  P.token_only = R_d > 0 && !has_dl;
+  udiv_consts((uint32_t)C, P.div_c);
+  udiv_consts((uint32_t)(ragged ? 1 : in->gamma + 1), P.div_g);
+  P.acc_len = out->accepted_len;
+  P.out_tokens = out->out_tokens;
+  P.p_draft = out->p_draft;
+  P.q_draft = out->q_draft;
+  P.beta = out->beta;
+  P.resid = out->resid_mass;
+  pl.K = kernels_for(cfg.dtype, vec, nper);
+  pl.ragged = ragged;
+  pl.has_dl = has_dl;
+  pl.wg = wg;
+  pl.R_t = R_t;
+  return SPECVERIFY_OK;
+}
+
+// The next epoch of a run on one workspace: never 0 (cleared memory carries
+// tag 0) and below 2^31 (the layout flag holds epoch * 2).
+uint32_t next_epoch(uint32_t& epoch) {
+  if (++epoch == 0 || epoch >= 0x80000000u) epoch = 1;
+  return epoch;
+}
+
+// Launch a planned run on stream (the current device is the workspace's).
+hipError_t launch_plan(Plan& pl, const Workspace& w, uint32_t epoch, hipStream_t stream) {
+  Params& P = pl.P;
+  P.xch1 = w.xch1;
+  P.dummy = w.dummy;
+  P.part = w.part;
+  P.rowinfo = pl.ragged ? w.rowinfo : nullptr;
+  P.layout = w.layout;
+  P.gbounds = pl.ragged ? w.gbounds : nullptr;
+  P.epoch = epoch;
+  if (pl.ragged)
+    hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, P, w.rowinfo, w.gbounds, w.layout);
+  hipLaunchKernelGGL(pl.has_dl ? pl.K.with_draft : pl.K.no_draft, dim3((uint32_t)(pl.wg * kGroups)),
+                     dim3(kStreamThreads), 0, stream, P);
+  return hipGetLastError();
+}
+
+// ================================================================== allocation-free runs
+
+// Zeroes n 16-byte words with vector stores.
+constexpr int kClearThreads = 256;
+__global__ __launch_bounds__(kClearThreads) void clear_kernel(uint4* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kClearThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kClearThreads)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Host state of specverify_run_static, per device.
+struct StaticDevice {
+  char* base;              // the device's copy of scratch (its device address); null until set up
+  uint32_t epoch;          // the last epoch used on the device
+  bool cap_known[2][3];    // [dtype][nper 1, 2, 4]
+  int cap[2][3][2][2];     // residency caps, as kernel_caps
+};
+constexpr int kStaticDevices = 64;
+std::mutex g_static_mu;
+StaticDevice g_static[kStaticDevices];
+
+}  // namespace
+
+// The workspace of specverify_run_static: a file-scope array that every
+// device the library is loaded on holds until the process ends.  In host
+// code its name stands for a host-side shadow, not for device memory: the
+// host uses only the address hipGetSymbolAddress returns for each device.
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / sizeof(uint64_t)];
+
+namespace {
+
+// Set up specverify_run_static on the current device (once per device):
+// the device's scratch address, and the scratch cleared on stream (tag 0 is
+// never an epoch).
+specverify_status static_setup(StaticDevice& d, hipStream_t stream) {
+  if (d.base) return SPECVERIFY_OK;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SPECVERIFY_ERR_DEVICE;
+  hipLaunchKernelGGL(clear_kernel, dim3(1024), dim3(kClearThreads), 0, stream, (uint4*)p,
+                     (int64_t)(kScratchBytes / sizeof(uint4)));
+  if (hipGetLastError() != hipSuccess) return SPECVERIFY_ERR_DEVICE;
+  d.base = (char*)p;
+  return SPECVERIFY_OK;
+}
+
+// specverify_run_static with its device current and the state lock held.
+specverify_status run_static_locked(const specverify_config& cfg, int C, const specverify_inputs* in,
+                                    const specverify_outputs* out, hipStream_t stream) {
+  StaticDevice& d = g_static[cfg.device];
+  specverify_status st = static_setup(d, stream);
+  if (st != SPECVERIFY_OK) return st;
+  const int nper = nper_for(C);
+  const int ni = nper == 1 ? 0 : nper == 2 ? 1 : 2;
+  if (!d.cap_known[cfg.dtype][ni]) {
+    int capmax = 0;
+    const hipError_t e = kernel_caps(cfg.dtype, nper, C, cfg.device, d.cap[cfg.dtype][ni], capmax);
+    if (e != hipSuccess) return e == hipErrorInvalidConfiguration ? SPECVERIFY_ERR_UNSUPPORTED : SPECVERIFY_ERR_DEVICE;
+    d.cap_known[cfg.dtype][ni] = true;
+  }
+  Plan pl;
+  const int64_t max_rows = (int64_t)cfg.max_batch * ((int64_t)cfg.max_gamma + 1);
+  st = plan_run(cfg, C, nper, max_rows, d.cap[cfg.dtype][ni], in, out, pl);
+  if (st != SPECVERIFY_OK || pl.R_t == 0) return st;
+  // this run's regions of the scratch, each on a 256-byte boundary
+  size_t end = 0;
+  auto take = [&end](size_t n) {
+    const size_t at = end;
+    end = (end + n + 255) & ~(size_t)255;
+    return at;
+  };
+  const size_t rc = (size_t)pl.R_t * (size_t)C;
+  const size_t o_x1 = take(rc * kX1 * sizeof(uint64_t));
+  const size_t o_part = take(rc * kPart * sizeof(float));
+  const size_t o_info = take((size_t)pl.R_t * sizeof(int4));
+  const size_t o_dummy = take((size_t)pl.wg * kGroups * kStreamWaves * 8 * sizeof(uint64_t));
+  const size_t o_layout = take(256);   // layout flag, group bounds at +64
+  if (end > kScratchBytes) return SPECVERIFY_ERR_TOO_LARGE;
+  const Workspace w{(uint64_t*)(d.base + o_x1),    (uint64_t*)(d.base + o_dummy), (float*)(d.base + o_part),
+                    (int4*)(d.base + o_info),       (uint32_t*)(d.base + o_layout),
+                    (int32_t*)(d.base + o_layout + 64)};
+  return launch_plan(pl, w, next_epoch(d.epoch), stream) == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_ERR_DEVICE;
+}
+
 }  // namespace
 
 struct specverify_ctx {
@@ -1725,21 +1996,14 @@ extern "C" {
 specverify_status specverify_create(const specverify_config* cfg, specverify_handle* out) {
   if (out) *out = nullptr;
   if (!cfg || !out) return SPECVERIFY_ERR_INVALID_ARGUMENT;
-  if (cfg->max_batch < 1 || cfg->max_gamma < 0 || cfg->max_gamma > kMaxGamma || cfg->vocab < 1 ||
-      cfg->spin_limit < 0 || (cfg->dtype != SPECVERIFY_F32 && cfg->dtype != SPECVERIFY_BF16))
-    return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  int C = 0;
+  const specverify_status cst = check_config(cfg, C);
+  if (cst != SPECVERIFY_OK) return cst;
   const int64_t rows = (int64_t)cfg->max_batch * ((int64_t)cfg->max_gamma + 1);
-  if (rows > (int64_t)1 << 24) return SPECVERIFY_ERR_INVALID_ARGUMENT;
-  const int C = chunks_for(cfg->vocab, cfg->dtype);
-  if (C > max_chunks(cfg->dtype)) return SPECVERIFY_ERR_UNSUPPORTED;
-  int ndev = 0;
-  if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev)
-    return SPECVERIFY_ERR_DEVICE;
   specverify_ctx* h = new (std::nothrow) specverify_ctx();
   if (!h) return SPECVERIFY_ERR_OUT_OF_MEMORY;
   h->cfg = *cfg;
-  if (h->cfg.spin_limit == 0) h->cfg.spin_limit = kDefaultSpin;
-  if (h->cfg.spin_limit > kMaxSpin) h->cfg.spin_limit = kMaxSpin;
+  h->cfg.spin_limit = spin_of(*cfg);
   h->chunks = C;
   h->nper = nper_for(C);
   h->rows = rows;
@@ -1749,29 +2013,8 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
     delete h;
     return SPECVERIFY_ERR_DEVICE;
   }
-  // Residency of the persistent grids: workgroups per CU times CUs.  With
-  // draft logits a row group needs at least C waves, so that the chunks of a
-  // row fall into one round or two consecutive ones and their waves meet in
-  // time.  A kernel that spilled to scratch would make the runtime allocate
-  // scratch at its first launch and spill in its inner loop: such a build is
-  // refused rather than run.
-  int cus = 0;
-  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cfg->device);
   int capmax = 0;
-  for (int v = 0; v < 4 && e == hipSuccess; ++v) {
-    const bool vec = (v & 1) == 1, dl = v < 2;
-    const Kernels K = kernels_for(cfg->dtype, vec, h->nper);
-    const void* fn = (const void*)(dl ? K.with_draft : K.no_draft);
-    hipFuncAttributes fa;
-    e = hipFuncGetAttributes(&fa, fn);
-    if (e == hipSuccess && fa.localSizeBytes > 0) e = hipErrorInvalidConfiguration;
-    int per_cu = 0;
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStreamThreads, 0);
-    h->cap[vec][dl] = cus * per_cu;
-    if (h->cap[vec][dl] > capmax) capmax = h->cap[vec][dl];
-    if (e == hipSuccess && (per_cu < 1 || (dl && (h->cap[vec][dl] / kGroups) * kStreamWaves < C)))
-      e = hipErrorInvalidConfiguration;
-  }
+  hipError_t e = kernel_caps(cfg->dtype, h->nper, C, cfg->device, h->cap, capmax);
   const size_t n1 = (size_t)rows * C * kX1 * sizeof(uint64_t);
   const size_t nd = (size_t)capmax * kStreamWaves * 8 * sizeof(uint64_t);   // dummy slots, per wave
   const size_t n2 = (size_t)rows * C * kPart * sizeof(float);
@@ -1808,117 +2051,44 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
 
 specverify_status specverify_run(specverify_handle h, const specverify_inputs* in,
                                  const specverify_outputs* out, void* hip_stream) {
-  if (!h || !in || !out) return SPECVERIFY_ERR_INVALID_ARGUMENT;
-  const int B = in->batch;
-  if (B < 0 || B > h->cfg.max_batch) return SPECVERIFY_ERR_INVALID_ARGUMENT;
-  if (B == 0) return SPECVERIFY_OK;
-  int64_t R_d;
-  if (in->cu_draft == nullptr) {
-    if (in->gamma < 0 || in->gamma > h->cfg.max_gamma) return SPECVERIFY_ERR_INVALID_ARGUMENT;
-    R_d = (int64_t)B * in->gamma;
-  } else {
-    if (in->num_draft_rows < 0) return SPECVERIFY_ERR_INVALID_ARGUMENT;
-    R_d = in->num_draft_rows;
-  }
-  const int64_t R_t = R_d + B;
-  if (R_t > h->rows) return SPECVERIFY_ERR_INVALID_ARGUMENT;
-  const int V = h->cfg.vocab;
-  if (!in->target_logits || !in->uniforms || !in->temperatures || !out->accepted_len ||
-      !out->out_tokens)
-    return SPECVERIFY_ERR_INVALID_ARGUMENT;
-  if (R_d > 0 && !in->draft_tokens) return SPECVERIFY_ERR_INVALID_ARGUMENT;
-  // drafts without logits are token-only drafts: q_i = delta_{x_i}
-  const bool has_dl = R_d > 0 && in->draft_logits != nullptr;
-  if (in->target_stride < V || (has_dl && in->draft_stride < V)) return SPECVERIFY_ERR_INVALID_ARGUMENT;
-  const int esize = h->cfg.dtype == SPECVERIFY_F32 ? 4 : 2;
-  if (in->target_stride * esize >= ((int64_t)1 << 31) || (has_dl && in->draft_stride * esize >= ((int64_t)1 << 31)))
-    return SPECVERIFY_ERR_UNSUPPORTED;   // row strides of 2 GB or more
-  if (((uintptr_t)in->target_logits % esize) || (has_dl && ((uintptr_t)in->draft_logits % esize)))
-    return SPECVERIFY_ERR_UNSUPPORTED;   // logits must be element aligned
-  // 16-byte loads need rows and the row length on 16-byte boundaries;
-  // otherwise the kernels read element by element.
-  const bool vec = !((uintptr_t)in->target_logits & 15) && !((in->target_stride * esize) & 15) &&
-                   !(((int64_t)V * esize) & 15) &&
-                   (!has_dl || (!((uintptr_t)in->draft_logits & 15) && !((in->draft_stride * esize) & 15)));
-
-  const bool ragged = in->cu_draft != nullptr;
-  const int C = h->chunks;
-  if (++h->epoch == 0) h->epoch = 1;   // 0 never tags a slot (workspace is zeroed)
-  if (h->epoch >= 0x80000000u) h->epoch = 1;   // the layout flag holds epoch * 2
-  Params P;
-  P.target = (const char*)in->target_logits;
-  P.draft = has_dl ? (const char*)in->draft_logits : nullptr;
-  P.tstride_b = (uint32_t)(in->target_stride * esize);
-  P.dstride_b = has_dl ? (uint32_t)(in->draft_stride * esize) : 0u;
-  P.tokens = in->draft_tokens;
-  P.uniforms = in->uniforms;
-  P.temps = in->temperatures;
-  P.cu_draft = in->cu_draft;
-  P.rowinfo = ragged ? h->rowinfo : nullptr;
-  P.layout = h->layout;
-  P.gbounds = ragged ? h->gbounds : nullptr;
-  // Row groups: contiguous ranges of whole sequences, about R_t / kGroups
-  // target rows each (for a ragged batch the layout kernel splits it).
-  int64_t rows_g;   // most target rows a group can get
-  if (!ragged) {
-    for (int g = 0; g <= kGroups; ++g) {
-      P.gseq[g] = (int32_t)(((int64_t)g * B) / kGroups);
-      P.grow[g] = P.gseq[g] * (in->gamma + 1);
-    }
-    rows_g = ((int64_t)(B + kGroups - 1) / kGroups) * (in->gamma + 1);
-  } else {
-    for (int g = 0; g <= kGroups; ++g) P.gseq[g] = P.grow[g] = 0;
-    rows_g = (R_t + kGroups - 1) / kGroups + h->cfg.max_gamma + 1;
-    if (rows_g > R_t) rows_g = R_t;
-  }
-  // Persistent grid: per row group, as many workgroups as the device holds,
-  // never more than the busiest group has items for.
-  const int64_t need = (rows_g * C + kStreamWaves - 1) / kStreamWaves;
-  int64_t wg = h->cap[vec ? 1 : 0][has_dl ? 1 : 0] / kGroups;
-  if (wg > need) wg = need;
-  if (wg < 1) wg = 1;
-  P.gamma = ragged ? 0 : in->gamma;
-  P.B = B;
-  P.R_d = (int32_t)R_d;
-  P.R_t = (int32_t)R_t;
-  P.V = V;
-  P.C = C;
-  P.Gw = (int32_t)(wg * kStreamWaves);
-  P.Wg = (int32_t)wg;
-  P.max_gamma = h->cfg.max_gamma;
-  P.epoch = h->epoch;
-  P.spin_limit = h->cfg.spin_limit;
-  P.token_only = R_d > 0 && !has_dl;
-  udiv_consts((uint32_t)C, P.div_c);
-  udiv_consts((uint32_t)(ragged ? 1 : in->gamma + 1), P.div_g);
-  P.xch1 = h->xch1;
-  P.dummy = h->dummy;
-  P.part = h->part;
-  P.acc_len = out->accepted_len;
-  P.out_tokens = out->out_tokens;
-  P.p_draft = out->p_draft;
-  P.q_draft = out->q_draft;
-  P.beta = out->beta;
-  P.resid = out->resid_mass;
+  if (!h) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  Plan pl;
+  const specverify_status st = plan_run(h->cfg, h->chunks, h->nper, h->rows, h->cap, in, out, pl);
+  if (st != SPECVERIFY_OK || pl.R_t == 0) return st;
+  const Workspace w{h->xch1, h->dummy, h->part, h->rowinfo, h->layout, h->gbounds};
+  const uint32_t epoch = next_epoch(h->epoch);
 
   int prev = 0;
   (void)hipGetDevice(&prev);
   if (prev != h->cfg.device && hipSetDevice(h->cfg.device) != hipSuccess) return SPECVERIFY_ERR_DEVICE;
   hipStream_t stream = (hipStream_t)hip_stream;
-  const Kernels K = kernels_for(h->cfg.dtype, vec, h->nper);
   hipError_t e = hipSuccess;
   hipEvent_t* ev = nullptr;
   if (h->timing && h->trec < SPECVERIFY_TIMING_RUNS) ev = h->ev + 3 * h->trec++;
   if (ev) e = hipEventRecord(ev[0], stream);
-  if (ragged)
-    hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, P, h->rowinfo, h->gbounds, h->layout);
-  hipLaunchKernelGGL(has_dl ? K.with_draft : K.no_draft, dim3((uint32_t)(wg * kGroups)), dim3(kStreamThreads), 0,
-                     stream, P);
+  const hipError_t e2 = launch_plan(pl, w, epoch, stream);
   if (ev && e == hipSuccess) e = hipEventRecord(ev[1], stream);
   if (ev && e == hipSuccess) e = hipEventRecord(ev[2], stream);
-  const hipError_t e2 = hipGetLastError();
   if (prev != h->cfg.device) (void)hipSetDevice(prev);
   return (e == hipSuccess && e2 == hipSuccess) ? SPECVERIFY_OK : SPECVERIFY_ERR_DEVICE;
+}
+
+specverify_status specverify_run_static(const specverify_config* cfg, const specverify_inputs* in,
+                                        const specverify_outputs* out, void* hip_stream) {
+  int C = 0;
+  const specverify_status cst = check_config(cfg, C);
+  if (cst != SPECVERIFY_OK) return cst;
+  if (cfg->device >= kStaticDevices) return SPECVERIFY_ERR_UNSUPPORTED;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  if (prev != cfg->device && hipSetDevice(cfg->device) != hipSuccess) return SPECVERIFY_ERR_DEVICE;
+  specverify_status st;
+  {
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    st = run_static_locked(*cfg, C, in, out, (hipStream_t)hip_stream);
+  }
+  if (prev != cfg->device) (void)hipSetDevice(prev);
+  return st;
 }
 
 specverify_status specverify_commit(specverify_handle h, const specverify_commit_args* a, void* hip_stream) {

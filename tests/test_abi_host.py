@@ -52,6 +52,17 @@ def test_null_arguments_rejected_without_device():
         assert lib.specverify_create(ctypes.byref(bad), ctypes.byref(h)) == binding.ERR_UNSUPPORTED
 
 
+def test_static_run_checks_its_config_without_device():
+    """specverify_run_static checks its configuration as create does, before
+    touching a device."""
+    lib = binding.load_library()
+    assert lib.specverify_run_static(None, None, None, None) == binding.ERR_INVALID_ARGUMENT
+    bad = binding.Config(0, 4, 1000, binding.BF16, 0, 0)          # max_batch 0
+    assert lib.specverify_run_static(ctypes.byref(bad), None, None, None) == binding.ERR_INVALID_ARGUMENT
+    bad = binding.Config(1, 4, 262144 + 1, binding.BF16, 0, 0)     # more than 128 bf16 chunks
+    assert lib.specverify_run_static(ctypes.byref(bad), None, None, None) == binding.ERR_UNSUPPORTED
+
+
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
@@ -72,3 +83,5 @@ def test_create_without_a_device_fails_cleanly():
     with pytest.raises(binding.SpecVerifyError) as e:
         binding.SpecVerify(max_batch=4, max_gamma=4, vocab=32000, dtype="f32")
     assert e.value.status == binding.ERR_DEVICE
+    # the allocation-free run fails the same way, before reading its inputs
+    assert lib.specverify_run_static(ctypes.byref(cfg), None, None, None) == binding.ERR_DEVICE
