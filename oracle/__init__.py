@@ -5,3 +5,4 @@ Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 """
 from .specverify_oracle import *  # noqa: F401,F403
 from .commit_oracle import commit_reference  # noqa: F401
+from .tree_oracle import *  # noqa: F401,F403

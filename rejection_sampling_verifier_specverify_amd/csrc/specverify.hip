@@ -1061,13 +1061,14 @@ __device__ __forceinline__ uint32_t row_payload(int status, bool acc, int tok) {
          (status == 0 ? ((uint32_t)tok & kTokMask) : 0u);
 }
 
+// a[j] for a wave-uniform j, by masks: a chain of selects can be turned
+// back into an indexed load from scratch memory
 template <int NPER>
 __device__ __forceinline__ float pick(const float (&a)[NPER], int j) {
-  float v = a[0];
+  uint32_t v = 0;
 #pragma unroll
-  for (int i = 1; i < NPER; ++i)
-    if (i == j) v = a[i];
-  return v;
+  for (int i = 0; i < NPER; ++i) v |= __float_as_uint(a[i]) & (0u - (uint32_t)(i == j));
+  return __uint_as_float(v);
 }
 
 // One logit of a row as fp32 (token t < V).
