@@ -19,7 +19,8 @@ stream.  Prints one JSON line.
 The same line carries: the per-step distribution (median, p10, p90), a
 warm-cache figure (no rotation), the device's streaming-read ceiling for the
 same bytes (the library's read probe), token-only drafts, the on-device
-commit, microseconds per call of every other workload, and the float64
+commit, microseconds per call of every other workload and of draft trees
+(60-node trees, B = 16), and the float64
 oracle timed on the host (one core, and a pool of worker processes).
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
@@ -504,6 +505,50 @@ def _workload_line(w, seed, dev, stream, steps):
     return res
 
 
+def _tree_line(name, seed, dev, stream, steps):
+    """Draft trees (specverify_run_tree): microseconds per call over rotating
+    copies, after a settle; outputs checked for shape."""
+    import torch
+    from rejection_sampling_verifier_specverify_amd.binding import SpecVerify
+    from rejection_sampling_verifier_specverify_amd.workloads import make_tree_inputs
+    inp = make_tree_inputs(name, seed)
+    B, N = inp.batch, int(inp.cu_nodes[-1])
+    R_t = N + B
+    w = inp.workload
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    logit_bytes = inp.target.nbytes
+    ncopy = max(1, int(np.ceil(2 * MALL_BYTES / logit_bytes)) + 1) if logit_bytes < 2 * MALL_BYTES else 1
+    t0 = up(inp.target)
+    copies = [t0] + [t0.clone() for _ in range(ncopy - 1)]
+    small = {k: up(getattr(inp, k)) for k in ("parents", "tokens", "uniforms", "temperatures", "cu_nodes")}
+    gmax = int(np.max(np.diff(inp.cu_nodes)))
+    sv = SpecVerify(max_batch=B, max_gamma=max(gmax, 1), vocab=w.vocab, dtype=w.dtype)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    toks = torch.empty(R_t, dtype=torch.int32, device=dev)
+    nodes = torch.empty(R_t, dtype=torch.int32, device=dev)
+
+    def step(k):
+        sv.run_tree(copies[k % ncopy], small["cu_nodes"], N, small["parents"], small["tokens"], small["uniforms"],
+                    small["temperatures"], acc, toks, out_nodes=nodes)
+
+    step(0)
+    torch.cuda.synchronize()
+    a = acc.cpu().numpy()
+    assert np.all((a >= 0) & (a <= np.diff(inp.cu_nodes))), a
+    _settle(step, stream, 0.05)
+    ms = _events_time(step, 0, steps, stream)
+    sv.close()
+    return dict(us_per_call=ms * 1e3, rows_per_s=R_t / (ms * 1e-3), logits_GBps=logit_bytes / (ms * 1e-3) / 1e9,
+                frac=logit_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, batch=B, nodes=N, rows_target=R_t,
+                vocab=w.vocab, logits=w.dtype, logit_bytes=logit_bytes, rotating_copies=ncopy,
+                mean_accepted_depth=float(np.mean(a)))
+
+
 def main():
     args = parse()
     if args.summarize_pmc or args.summarize_trace or args.summarize_sq:
@@ -601,6 +646,8 @@ def main():
             if name != w.name:
                 others[name] = _workload_line(ow, args.seed, dev, stream, 100)
                 torch.cuda.empty_cache()
+        others["tree_b16_tree60_v128256_bf16"] = _tree_line("b16_tree60_v128256_bf16", args.seed, dev, stream, 100)
+        torch.cuda.empty_cache()
 
     # one launch per step: the launches' average duration is the timed
     # region's elapsed time over K (back-to-back launches on one stream)

@@ -148,6 +148,58 @@ specverify_status specverify_create(const specverify_config* cfg, specverify_han
 specverify_status specverify_run(specverify_handle h, const specverify_inputs* in,
                                  const specverify_outputs* out, void* hip_stream);
 
+/* Verification over a draft tree (Perplexity "Accelerating Sonar through
+ * speculation", sections "추측적 디코딩", stage 2, and "EAGLE": the drafter
+ * explores a tree and keeps its Top-K candidates at every node).  The pages
+ * give no rule for several candidates of one node; this library reads each
+ * candidate as a token-only draft (q = delta_c) and applies the chain's rule
+ * per candidate: the children of the current node are tested in node order,
+ * candidate c accepted when u_c < r(c), r the node's target distribution
+ * with the candidates rejected so far removed and renormalised (velog
+ * "6-1편. Speculative Decoding", section 2-1 with q = delta_c, and the
+ * residual of section 2-2); an accepted candidate is emitted and the walk
+ * continues at it; when every child is rejected, or at a leaf, the final
+ * token is sampled from that residual (inverse CDF in token order).  T = 0:
+ * the first child equal to its node's target argmax; else the argmax.
+ *
+ * Layout, per sequence b with N_b drafted nodes (numbered 1 .. N_b; node 0
+ * is the root, the last committed token): nodes cu_nodes[b] ..
+ * cu_nodes[b+1] - 1 of parents[] and tokens[]; parents[cu_nodes[b] + k - 1]
+ * is node k's parent, in [0, k - 1]; target rows and uniforms at
+ * cu_t[b] = cu_nodes[b] + b: row cu_t[b] + k is the target distribution
+ * after node k (k = 0: after the root); uniforms[cu_t[b] + k - 1] tests
+ * node k and uniforms[cu_t[b] + N_b] drives the final sample.  A chain
+ * (node k's parent k - 1) is exactly specverify_run with token-only drafts.
+ * Invalid data (the chain case's rules, a parent outside [0, k - 1]) gives
+ * accepted_len -1 and -1 outputs.  Limits: N_b <= max_gamma, R_t = N + B <=
+ * max_batch * (max_gamma + 1).  One kernel launch after the layout check. */
+typedef struct {
+  int32_t batch;              /* B >= 0                                            */
+  const int32_t* cu_nodes;    /* [B+1] node offsets (device), cu_nodes[0] = 0      */
+  int32_t num_nodes;          /* N = cu_nodes[B] (host copy)                       */
+  const int32_t* parents;     /* [N] parent of each node, local index (device)     */
+  const int32_t* tokens;      /* [N] each node's candidate token (device)          */
+  const void* target_logits;  /* [R_t, target_stride] f32 or bf16, R_t = N + B     */
+  int64_t target_stride;      /* elements between rows, >= V                       */
+  const float* uniforms;      /* [R_t] u in [0, 1)                                 */
+  const float* temperatures;  /* [B] T_b; 0 = greedy                               */
+} specverify_tree_inputs;
+
+typedef struct {
+  int32_t* accepted_len;      /* [B] n_b, the accepted depth; -1 invalid; -2 wait expired */
+  int32_t* out_tokens;        /* [R_t] at cu_t[b] + j: the j-th accepted node's token for
+                                 j < n_b, the final token at j = n_b, -1 after            */
+  int32_t* out_nodes;         /* [R_t] at cu_t[b] + j: the j-th accepted node (1-based) for
+                                 j < n_b, -1 after; or NULL                               */
+  float* p_cand;              /* [N] each candidate's p under its parent's target row (T = 0:
+                                 1 if it is the argmax, else 0); NaN if invalid; or NULL */
+} specverify_tree_outputs;
+
+/* Errors as specverify_run (no launch happens): INVALID_ARGUMENT also for
+ * NULL cu_nodes (B > 0) or NULL parents / tokens (N > 0). */
+specverify_status specverify_run_tree(specverify_handle h, const specverify_tree_inputs* in,
+                                      const specverify_tree_outputs* out, void* hip_stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * run as specverify_run, with the same kernels, results, arguments and

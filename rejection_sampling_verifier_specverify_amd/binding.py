@@ -26,7 +26,7 @@ MAX_CHUNKS = {"bf16": 128, "f32": 256}
 EXPORTED = ("specverify_create", "specverify_run", "specverify_destroy",
             "specverify_set_timing", "specverify_timing_totals",
             "specverify_chunks_per_row", "specverify_workspace_bytes", "specverify_commit",
-            "specverify_probe_read", "specverify_run_static")
+            "specverify_probe_read", "specverify_run_static", "specverify_run_tree")
 
 
 class Config(ctypes.Structure):
@@ -48,6 +48,18 @@ class Outputs(ctypes.Structure):
     _fields_ = [("accepted_len", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
                 ("p_draft", ctypes.c_void_p), ("q_draft", ctypes.c_void_p),
                 ("beta", ctypes.c_void_p), ("resid_mass", ctypes.c_void_p)]
+
+
+class TreeInputs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("cu_nodes", ctypes.c_void_p), ("num_nodes", ctypes.c_int32),
+                ("parents", ctypes.c_void_p), ("tokens", ctypes.c_void_p),
+                ("target_logits", ctypes.c_void_p), ("target_stride", ctypes.c_int64),
+                ("uniforms", ctypes.c_void_p), ("temperatures", ctypes.c_void_p)]
+
+
+class TreeOutputs(ctypes.Structure):
+    _fields_ = [("accepted_len", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
+                ("out_nodes", ctypes.c_void_p), ("p_cand", ctypes.c_void_p)]
 
 
 class CommitArgs(ctypes.Structure):
@@ -93,6 +105,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.specverify_run_static.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Inputs), ctypes.POINTER(Outputs),
                                           ctypes.c_void_p]
     lib.specverify_run_static.restype = ctypes.c_int
+    lib.specverify_run_tree.argtypes = [ctypes.c_void_p, ctypes.POINTER(TreeInputs), ctypes.POINTER(TreeOutputs),
+                                        ctypes.c_void_p]
+    lib.specverify_run_tree.restype = ctypes.c_int
     lib.specverify_destroy.argtypes = [ctypes.c_void_p]
     lib.specverify_destroy.restype = ctypes.c_int
     lib.specverify_chunks_per_row.argtypes = [ctypes.c_void_p]
@@ -134,6 +149,12 @@ def specverify_run_static(cfg: Config, inputs: Inputs, outputs: Outputs, stream:
                                               ctypes.c_void_p(stream))
     if st != OK:
         raise SpecVerifyError("specverify_run_static", st)
+
+
+def specverify_run_tree(h: ctypes.c_void_p, inputs: TreeInputs, outputs: TreeOutputs, stream: int) -> None:
+    st = load_library().specverify_run_tree(h, ctypes.byref(inputs), ctypes.byref(outputs), ctypes.c_void_p(stream))
+    if st != OK:
+        raise SpecVerifyError("specverify_run_tree", st)
 
 
 def specverify_commit(h: ctypes.c_void_p, args: CommitArgs, stream: int) -> None:
@@ -229,6 +250,44 @@ def check_run_args(*, vocab, logits_dtype, device, target, draft, draft_tokens, 
     for name, t in diagnostics:
         _check_vec(name, t, torch.float32, device, R_d, required=False)
     return B, R_d, R_t
+
+
+def check_tree_args(*, vocab, logits_dtype, device, target, cu_nodes, num_nodes, parents, tokens, uniforms,
+                    temperatures, accepted_len, out_tokens, out_nodes=None, p_cand=None):
+    """The tensors of one tree run (see specverify_run_tree): checked as
+    check_run_args does.  Returns (B, N, R_t)."""
+    import torch
+    if temperatures is None or temperatures.dim() != 1:
+        raise ValueError("temperatures must be a 1-D tensor of B float32 values")
+    B = int(temperatures.shape[0])
+    N = int(num_nodes)
+    if N < 0:
+        raise ValueError("num_nodes must be >= 0")
+    R_t = N + B
+    _check_vec("cu_nodes", cu_nodes, torch.int32, device, B + 1)
+    if target is None:
+        if R_t > 0:
+            raise ValueError("target logits are required")
+    else:
+        if target.dtype != logits_dtype:
+            raise TypeError(f"target logits must be {logits_dtype}, got {target.dtype}")
+        if target.device != device:
+            raise ValueError(f"target logits must be on {device}, got {target.device}")
+        if target.dim() != 2 or target.stride(1) != 1:
+            raise ValueError("target logits must be a 2-D tensor with unit column stride")
+        if target.shape[1] < vocab or target.stride(0) < vocab:
+            raise ValueError(f"target logits rows must hold the vocabulary ({vocab})")
+        if target.shape[0] < R_t:
+            raise ValueError(f"target logits have {target.shape[0]} rows, the run needs {R_t}")
+    _check_vec("parents", parents, torch.int32, device, N)
+    _check_vec("tokens", tokens, torch.int32, device, N)
+    _check_vec("uniforms", uniforms, torch.float32, device, R_t)
+    _check_vec("temperatures", temperatures, torch.float32, device, B)
+    _check_vec("accepted_len", accepted_len, torch.int32, device, B)
+    _check_vec("out_tokens", out_tokens, torch.int32, device, R_t)
+    _check_vec("out_nodes", out_nodes, torch.int32, device, R_t, required=False)
+    _check_vec("p_cand", p_cand, torch.float32, device, N, required=False)
+    return B, N, R_t
 
 
 def check_commit_args(*, device, accepted_len, out_tokens, seq_tokens, seq_lens, gamma=None, cu_draft=None,
@@ -355,6 +414,23 @@ class SpecVerify:
                                    out_tokens, gamma, cu_draft, num_draft_rows, p_draft, q_draft, beta,
                                    resid_mass, stream)
         specverify_run(self.handle, inp, out, s)
+
+    def run_tree(self, target, cu_nodes, num_nodes: int, parents, tokens, uniforms, temperatures, accepted_len,
+                 out_tokens, *, out_nodes=None, p_cand=None, stream=None) -> None:
+        """Verification over draft trees (specverify_run_tree), on the current
+        torch stream; returns without synchronising."""
+        import torch
+        want = torch.float32 if self.dtype == F32 else torch.bfloat16
+        B, N, _ = check_tree_args(
+            vocab=self.vocab, logits_dtype=want, device=torch.device("cuda", self.device), target=target,
+            cu_nodes=cu_nodes, num_nodes=num_nodes, parents=parents, tokens=tokens, uniforms=uniforms,
+            temperatures=temperatures, accepted_len=accepted_len, out_tokens=out_tokens, out_nodes=out_nodes,
+            p_cand=p_cand)
+        inp = TreeInputs(B, _ptr(cu_nodes), N, _ptr(parents) if N > 0 else None, _ptr(tokens) if N > 0 else None,
+                         _ptr(target), int(target.stride(0)), _ptr(uniforms), _ptr(temperatures))
+        out = TreeOutputs(_ptr(accepted_len), _ptr(out_tokens), _ptr(out_nodes), _ptr(p_cand))
+        s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
+        specverify_run_tree(self.handle, inp, out, int(s))
 
     def commit(self, accepted_len, out_tokens, seq_tokens, seq_lens, *, gamma: Optional[int] = None,
                cu_draft=None, num_draft_rows: Optional[int] = None, appended=None, next_token=None,

@@ -158,6 +158,11 @@ struct Params {
   float* q_draft;
   float* beta;
   float* resid;
+  // draft trees (token-only candidates): node parents, and the extra outputs
+  int32_t tree;
+  const int32_t* parents;    // [R_d] parent of each drafted node, local (0 = root)
+  int32_t* out_nodes;        // [R_t] accepted nodes in path order, or NULL
+  float* p_cand;             // [R_d] each candidate under its parent's target distribution, or NULL
 };
 
 // ------------------------------------------------------------------ slots
@@ -632,7 +637,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(Params P, int4* 
     for (int b = tid; b < P.B; b += blockDim.x) {
       const int d0 = P.cu_draft[b], g = P.cu_draft[b + 1] - d0;
       const int Tb = __float_as_int(P.temps[b]);
-      for (int i = 0; i <= g; ++i) rowinfo[d0 + b + i] = make_int4(b, d0 + i, i < g ? 1 : 0, Tb);
+      // a tree's rows have no draft to test in the streaming pass
+      for (int i = 0; i <= g; ++i) rowinfo[d0 + b + i] = make_int4(b, d0 + i, (i < g && !P.tree) ? 1 : 0, Tb);
     }
     if (tid <= kGroups) {
       // first sequence whose first target row reaches tid * R_t / kGroups
@@ -1486,14 +1492,352 @@ __device__ __forceinline__ void invalid_batch(const Params& P) {
   for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < n; t += gridDim.x * blockDim.x) {
     if (t < P.B) P.acc_len[t] = -1;
     if (t < P.R_t) P.out_tokens[t] = -1;
+    if (t < P.R_t && P.out_nodes) P.out_nodes[t] = -1;
+    if (t < P.R_d && P.p_cand) P.p_cand[t] = __builtin_nanf("");
   }
+}
+
+// ================================================================== resolution of a draft tree
+
+// Sampling inside the owner chunk cs of a tree node's row (in R[0]): the
+// first token whose cumulative weight, in the chunk's units, exceeds tau;
+// the weights are the chunk's e_t, and 0 at the rejected candidates' tokens
+// (nrem of them in rtok).  Token order, as sample_scan.
+template <int DT>
+__device__ __forceinline__ int tree_scan(const Params& P, int cs, float tau, float ct, float s, const int* rtok,
+                                         int nrem, int lane, u32x4 (&R)[2][kU]) {
+  using F = Fmt<DT>;
+  if ((cs + 1) * F::CH > P.V) mask_raw<DT>(R[0], cs, P.V, lane);   // tokens >= V: weight 0
+  int first = 0x7FFFFFFF, lastpos = -1;
+  float rbase = 0.0f;
+#pragma unroll 1
+  for (int u = 0; u < kU; ++u) {
+    u32x4 vt = R[0][0];
+#pragma unroll
+    for (int i = 1; i < kU; ++i) vt = i == u ? R[0][i] : vt;
+    float w[F::EPV];
+#pragma unroll
+    for (int e = 0; e < F::EPV; ++e) w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(vt, e), s, ct));
+    for (int j = 0; j < nrem; ++j) {
+      const int t = rtok[j] - (cs * F::CH + u * 64 * F::EPV + lane * F::EPV);   // its element in this lane
+#pragma unroll
+      for (int e = 0; e < F::EPV; ++e) w[e] = t == e ? 0.0f : w[e];
+    }
+    float loc[F::EPV];
+    float run = 0.0f;
+#pragma unroll
+    for (int e = 0; e < F::EPV; ++e) {
+      run += w[e];
+      loc[e] = run;
+    }
+    const float incl = wave_scan(run, lane);
+    const float excl = rbase + (incl - run);
+    int cand = 0x7FFFFFFF;
+#pragma unroll
+    for (int e = F::EPV - 1; e >= 0; --e) {
+      const int k = u * 64 * F::EPV + lane * F::EPV + e;
+      if (w[e] > 0.0f) {
+        if (excl + loc[e] > tau) cand = k;
+        lastpos = max(lastpos, k);
+      }
+    }
+    if (__ballot(cand != 0x7FFFFFFF)) {
+      first = wave_min_i(cand);
+      break;
+    }
+    rbase = rbase + lane_f(incl, 63);
+  }
+  if (first == 0x7FFFFFFF) lastpos = wave_max_i(lastpos);
+  const int pickk = first != 0x7FFFFFFF ? first : lastpos;
+  const int tok = cs * F::CH + pickk;
+  return (pickk < 0 || tok >= P.V) ? -1 : tok;
+}
+
+// The slots of row r once all carry this run's tag (the wait ends: the help
+// computes missing chunks itself).  False: the bounded wait expired.
+template <int DT, bool VEC, int NPER>
+__device__ __forceinline__ bool tree_poll(const Params& P, int r, int mode, float s, int lane,
+                                          const uint32_t (&soff)[NPER], RowSlots<NPER>& q) {
+  for (int k = 0;; ++k) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the loads below are read again on every turn
+    slots_issue(P, r, true, soff, q);
+    if (slots_ready(q, P.C, P.epoch, lane)) return true;
+    if (k > 2 * P.spin_limit + 16) return false;
+    if (k == P.spin_limit) {
+      help_slots<DT, VEC, false, NPER>(P, r, 0, mode, false, false, s, lane, q);
+      __builtin_amdgcn_s_waitcnt(0);   // its stores are in L2 before the poll below
+    } else {
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+}
+
+// m of chunk cx (lane-varying) from the row's slots: slot 0 of chunk cx
+// sits in lane cx mod 64 of the lane's array cx / 64.
+template <int NPER>
+__device__ __forceinline__ float chunk_m_of(const RowSlots<NPER>& q, int cx) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((cx & 63) * 4, (int)(uint32_t)q.w[j][0]);
+    v = (cx >> 6) == j ? w : v;
+  }
+  return __uint_as_float(v);
+}
+
+// One sequence whose N drafts form a tree (token-only candidates), on one
+// workgroup.  Perplexity "Accelerating Sonar through speculation", section
+// "EAGLE" (Top-K candidates per node), with velog "6-1편. Speculative
+// Decoding", sections 2-1 and 2-2 applied per candidate with q = delta_c:
+// the children of the current node are tested in node order against the
+// node's residual (p with the rejected candidates removed, renormalised);
+// an accepted candidate is emitted and the walk moves to it; when all are
+// rejected, or at a leaf, the final token is sampled from the residual by
+// inverse CDF in token order.  T = 0: the child equal to the row's argmax.
+//   1. nodes into LDS, checked, children lists (siblings in node order);
+//   2. the four waves poll the rows (row v on wave v mod 4) and compute
+//      each candidate's p under its parent's row (the logit at its token
+//      with its chunk's offset and scale, as the streaming pass formed it);
+//   3. wave 0 walks the tree in LDS, then samples the final token.
+template <int DT, bool VEC, int NPER>
+__device__ __forceinline__ void resolve_tree(const Params& P, int b, int lane, int wv) {
+  using F = Fmt<DT>;
+  __shared__ int tpar[kMaxGamma + 1];    // node k's parent, k >= 1
+  __shared__ int ttok[kMaxGamma + 1];    // node k's candidate
+  __shared__ int toff[kMaxGamma + 2];    // children of node v: tlist[toff[v] .. toff[v+1])
+  __shared__ int tlist[kMaxGamma + 1];
+  __shared__ float tprob[kMaxGamma + 1]; // p of node k's candidate under its parent's row
+  __shared__ int tamax[kMaxGamma + 1];   // greedy: each row's argmax
+  __shared__ int tpath[kMaxGamma + 1];
+  __shared__ int trem[kMaxGamma + 1];    // the rejected candidates' tokens at the last node
+  __shared__ float trp[kMaxGamma + 1];   // ... and the probability each removed
+  __shared__ int tst;                    // worst row status
+  const int tid = threadIdx.x;
+  const int n0 = ld_const(P.cu_draft, b);
+  const int N = ld_const(P.cu_draft, b + 1) - n0;   // in [0, max_gamma]: the layout was checked
+  const int t0 = n0 + b;
+  const float T = ld_const(P.temps, b);
+  const bool sampled = t_sampled(T);
+  const float s = sampled ? kLog2e / T : 0.0f;
+  int bad = !(sampled || T == 0.0f);
+  for (int k = tid + 1; k <= N; k += kStreamThreads) {
+    const int pa = P.parents[n0 + k - 1], tk = P.tokens[n0 + k - 1];
+    bad |= pa < 0 || pa >= k || tk < 0 || tk >= P.V;
+    tpar[k] = pa;
+    ttok[k] = tk;
+  }
+  for (int k = tid; k <= N; k += kStreamThreads) bad |= !u_ok(P.uniforms[t0 + k]);
+  if (tid == 0) {
+    tst = 0;
+    tpar[0] = 0;
+    ttok[0] = 0;
+  }
+  bad = __syncthreads_or(bad);
+  if (!bad) {
+    // children lists: node k goes to slot toff[parent] + (its rank among its siblings)
+    for (int v = tid; v <= N + 1; v += kStreamThreads) {
+      int o = 0;
+      for (int k = 1; k <= N; ++k) o += tpar[k] < v;
+      toff[v] = o;
+    }
+    __syncthreads();
+    for (int k = tid + 1; k <= N; k += kStreamThreads) {
+      const int pa = tpar[k];
+      int rank = 0;
+      for (int k2 = 1; k2 < k; ++k2) rank += tpar[k2] == pa;
+      tlist[toff[pa] + rank] = k;
+    }
+    __syncthreads();
+    // the rows
+    uint32_t soff[NPER];
+    chunk_offsets(P.C, lane, kX1 * (int)sizeof(uint64_t), soff);
+    int rowbad = 0;
+    for (int v = wv; v <= N; v += kStreamWaves) {
+      const int r = t0 + v;
+      const int c0 = toff[v], c1 = toff[v + 1];
+      // the logits at the first 64 candidates go out before the poll
+      const int k0 = c0 + lane < c1 ? tlist[c0 + lane] : 0;
+      float l0 = 0.0f;
+      if (sampled && c0 + lane < c1) l0 = load_logit<DT>(P.target, r, P.tstride_b, ttok[k0]);
+      RowSlots<NPER> q;
+      if (!tree_poll<DT, VEC, NPER>(P, r, sampled ? 1 : 2, s, lane, soff, q)) {
+        rowbad = max(rowbad, 2);
+        continue;
+      }
+      if (sampled) {
+        float M, S;
+        merge_row(q, P.C, 0, s, lane, M, S);
+        if (!norm_ok(M, S)) {
+          rowbad = max(rowbad, 1);
+          continue;
+        }
+        for (int i0 = c0; i0 < c1; i0 += 64) {
+          const int i = i0 + lane;
+          const int k = i < c1 ? tlist[i] : 0;
+          const int x = ttok[k];
+          const float l = i0 == c0 ? l0 : (i < c1 ? load_logit<DT>(P.target, r, P.tstride_b, x) : 0.0f);
+          const float mx = chunk_m_of(q, i < c1 ? x / F::CH : 0);
+          const float px =
+              chunk_scale(mx, M, S, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(l, s, chunk_offset(mx, s)));
+          if (i < c1) tprob[k] = px;
+        }
+      } else {
+        float av = -__builtin_huge_valf();
+        int ak = 0x7FFFFFFF, gb = 0;
+#pragma unroll
+        for (int j = 0; j < NPER; ++j) {
+          if (lane + 64 * j < P.C) {
+            argmax_merge(av, ak, slot_f(q.w[j][0]), (int)(uint32_t)q.w[j][1]);
+            gb |= (uint32_t)q.w[j][1] == 0xFFFFFFFFu;
+          }
+        }
+        gb = __any(gb);
+        wave_argmax(av, ak);
+        if (gb || av == -__builtin_huge_valf()) {
+          rowbad = max(rowbad, 1);
+          continue;
+        }
+        if (lane == 0) tamax[v] = ak;
+        for (int i = c0 + lane; i < c1; i += 64) tprob[tlist[i]] = ttok[tlist[i]] == ak ? 1.0f : 0.0f;
+      }
+    }
+    if (lane == 0 && rowbad) atomicMax(&tst, rowbad);
+    __syncthreads();
+    bad = tst;
+  }
+  if (wv == 0) {
+    int n = 0, tok = -1;
+    if (!bad) {
+      // the walk
+      int v = 0, nr = 0;
+      for (;;) {
+        const int c0 = toff[v], c1 = toff[v + 1];
+        int nxt = -1;
+        float rem = 0.0f;
+        nr = 0;
+        for (int i = c0; i < c1; ++i) {
+          const int k = tlist[i];
+          const int x = ttok[k];
+          bool acc;
+          float p = 0.0f;
+          if (sampled) {
+            p = tprob[k];
+            for (int j = 0; j < nr; ++j) p = trem[j] == x ? 0.0f : p;   // a token already removed has p 0
+            acc = ld_const(P.uniforms, t0 + k - 1) * (1.0f - rem) < p;
+          } else {
+            acc = x == tamax[v];
+          }
+          if (acc) {
+            nxt = k;
+            break;
+          }
+          rem += p;
+          trem[nr] = x;   // every lane writes the same value: each reads its own write
+          trp[nr] = p;
+          ++nr;
+        }
+        if (nxt < 0) break;
+        tpath[n] = nxt;
+        ++n;
+        v = nxt;
+      }
+      if (!sampled) {
+        tok = tamax[v];
+      } else {
+        // the final sample at v: the row's chunk masses less the removed candidates'
+        const int r = t0 + v;
+        uint32_t soff[NPER];
+        chunk_offsets(P.C, lane, kX1 * (int)sizeof(uint64_t), soff);
+        RowSlots<NPER> q;
+        if (!tree_poll<DT, VEC, NPER>(P, r, 1, s, lane, soff, q)) {
+          bad = 2;
+        } else {
+          float M, S;
+          merge_row(q, P.C, 0, s, lane, M, S);
+          float at[NPER], mt[NPER], tot[NPER];
+          for (int pass = 0;; ++pass) {
+            float ml = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < NPER; ++jj) {
+              const int c = lane + 64 * jj;
+              const bool inr = c < P.C;
+              mt[jj] = inr ? slot_f(q.w[jj][0]) : -__builtin_huge_valf();
+              at[jj] = inr ? chunk_scale(mt[jj], M, S, s) : 0.0f;
+              float t = inr ? at[jj] * slot_f(q.w[jj][1]) : 0.0f;
+              for (int j = 0; j < nr; ++j) t -= (inr && trem[j] / F::CH == c) ? trp[j] : 0.0f;
+              tot[jj] = fmaxf(t, 0.0f);
+              ml += tot[jj];
+            }
+            const float mass = wave_sum(ml);
+            if (mass > 0.0f || nr == 0 || pass > 0) {
+              // owner chunk: the first whose cumulative mass exceeds thr (rounding guard: the last with mass)
+              const float thr = ld_const(P.uniforms, t0 + N) * mass;
+              int cs = -1, last = -1;
+              float before = 0.0f, last_before = 0.0f, base = 0.0f;
+#pragma unroll
+              for (int jj = 0; jj < NPER; ++jj) {
+                const bool inr = lane + 64 * jj < P.C;
+                const float t = inr ? tot[jj] : 0.0f;
+                const float Gs = base + wave_scan(t, lane);
+                const float Gex = Gs - t;
+                const uint64_t hit = __ballot(inr && t > 0.0f && Gs > thr);
+                const uint64_t pos = __ballot(inr && t > 0.0f);
+                if (cs < 0 && hit) {
+                  const int l = __builtin_ctzll(hit);
+                  cs = 64 * jj + l;
+                  before = lane_f(Gex, l);
+                }
+                if (pos) {
+                  const int l = 63 - __builtin_clzll(pos);
+                  last = 64 * jj + l;
+                  last_before = lane_f(Gex, l);
+                }
+                base = lane_f(Gs, 63);
+              }
+              if (cs < 0) {
+                cs = last;
+                before = last_before;
+              }
+              if (cs < 0) {
+                bad = 2;
+              } else {
+                const int ls = cs & 63, js = cs >> 6;
+                const float tau = (thr - before) / lane_f(pick(at, js), ls);
+                const float ct = chunk_offset(lane_f(pick(mt, js), ls), s);
+                u32x4 R[2][kU];
+                const int nb = P.V * F::ESIZE;
+                issue_row<DT, VEC>(chunk_rsrc(P.target, r, P.tstride_b, cs, nb, true), lane, R[0]);
+                tok = tree_scan<DT>(P, cs, tau, ct, s, trem, nr, lane, R);
+                if (tok < 0) bad = 2;
+              }
+              break;
+            }
+            --nr;   // every mass removed (rounding): the residual before the last removal
+          }
+        }
+      }
+    }
+    // outputs: the path's tokens and nodes, the final token, -1 after
+    for (int j0 = 0; j0 <= N; j0 += 64) {
+      const int j = j0 + lane;
+      if (j <= N) {
+        const int node = min(max(tpath[min(j, kMaxGamma)], 0), kMaxGamma);   // read for j < n only
+        P.out_tokens[t0 + j] = (bad || j > n) ? -1 : j < n ? ttok[node] : tok;
+        if (P.out_nodes) P.out_nodes[t0 + j] = (bad || j >= n) ? -1 : node;
+      }
+    }
+    if (P.p_cand)
+      for (int k = 1 + lane; k <= N; k += 64) P.p_cand[n0 + k - 1] = bad ? __builtin_nanf("") : tprob[k];
+    if (lane == 0) P.acc_len[b] = bad == 2 ? -2 : bad ? -1 : n;
+  }
+  __syncthreads();   // the LDS arrays are reused by the next sequence
 }
 
 // ================================================================== the kernel
 
 // D: the launch has draft logits (two-phase pipeline); otherwise phase 1
 // alone, with the next item's loads in flight.
-template <int DT, bool VEC, int NPER, bool D>
+template <int DT, bool VEC, int NPER, bool D, bool TREE = false>
 __global__ __launch_bounds__(kStreamThreads, D ? 2 : 1) void verify_kernel(Params P) {
   using F = Fmt<DT>;
   __shared__ uint32_t shres[kMaxGamma + 1];
@@ -1574,7 +1918,10 @@ __global__ __launch_bounds__(kStreamThreads, D ? 2 : 1) void verify_kernel(Param
   // The last workgroups of a group stream one item fewer per wave when the
   // items do not divide evenly, so they finish streaming first.
   const int nseq = Gr.s1 - Gr.s0;
-  for (int k = P.Wg - 1 - wgl; k < nseq; k += P.Wg) resolve_sequence<DT, VEC, D, NPER>(P, Gr.s0 + k, lane, wave, shres);
+  for (int k = P.Wg - 1 - wgl; k < nseq; k += P.Wg) {
+    if constexpr (TREE) resolve_tree<DT, VEC, NPER>(P, Gr.s0 + k, lane, wave);
+    else resolve_sequence<DT, VEC, D, NPER>(P, Gr.s0 + k, lane, wave, shres);
+  }
 }
 
 // ================================================================== commit kernel
@@ -1672,17 +2019,25 @@ __global__ __launch_bounds__(kProbeThreads) void probe_kernel(const char* a, int
 // ================================================================== launch table
 
 typedef void (*KernelFn)(Params);
+// The three launches of a build: with draft logits, without (token-only
+// drafts, or none), and draft trees (token-only candidates).
+enum { kNoDraft = 0, kDraft = 1, kTree = 2 };
 struct Kernels {
-  KernelFn with_draft, no_draft;   // no_draft: launches without draft logits
+  KernelFn fn[3];
 };
+template <int DT, bool VEC, int NPER>
+Kernels kernels_of() {
+  return {{verify_kernel<DT, VEC, NPER, false>, verify_kernel<DT, VEC, NPER, true>,
+           verify_kernel<DT, VEC, NPER, false, true>}};
+}
 template <int DT, bool VEC>
 Kernels kernels_for(int nper) {
-  if (nper == 1) return {verify_kernel<DT, VEC, 1, true>, verify_kernel<DT, VEC, 1, false>};
-  if (nper == 2) return {verify_kernel<DT, VEC, 2, true>, verify_kernel<DT, VEC, 2, false>};
+  if (nper == 1) return kernels_of<DT, VEC, 1>();
+  if (nper == 2) return kernels_of<DT, VEC, 2>();
   // more than 128 chunks per row: fp32 only (the bf16 build would not fit
   // its registers)
-  if constexpr (DT == SPECVERIFY_F32) return {verify_kernel<DT, VEC, 4, true>, verify_kernel<DT, VEC, 4, false>};
-  return {nullptr, nullptr};
+  if constexpr (DT == SPECVERIFY_F32) return kernels_of<DT, VEC, 4>();
+  return {{nullptr, nullptr, nullptr}};
 }
 Kernels kernels_for(int dtype, bool vec, int nper) {
   if (dtype == SPECVERIFY_F32) return vec ? kernels_for<SPECVERIFY_F32, true>(nper) : kernels_for<SPECVERIFY_F32, false>(nper);
@@ -1723,28 +2078,27 @@ int spin_of(const specverify_config& cfg) {
 }
 
 // Residency of the persistent grids of a (dtype, nper) build on the current
-// device: workgroups per CU times CUs, [vector loads][draft logits].  With
+// device: workgroups per CU times CUs, [vector loads][kind of launch].  With
 // draft logits a row group needs at least C waves, so that the chunks of a
 // row fall into one round or two consecutive ones and their waves meet in
 // time.  A kernel that spilled to scratch would make the runtime allocate
 // scratch at its first launch and spill in its inner loop: such a build is
 // refused rather than run (hipErrorInvalidConfiguration).
-hipError_t kernel_caps(int dtype, int nper, int C, int device, int (&cap)[2][2], int& capmax) {
+hipError_t kernel_caps(int dtype, int nper, int C, int device, int (&cap)[2][3], int& capmax) {
   int cus = 0;
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   capmax = 0;
-  for (int v = 0; v < 4 && e == hipSuccess; ++v) {
-    const bool vec = (v & 1) == 1, dl = v < 2;
-    const Kernels K = kernels_for(dtype, vec, nper);
-    const void* fn = (const void*)(dl ? K.with_draft : K.no_draft);
+  for (int v = 0; v < 6 && e == hipSuccess; ++v) {
+    const int vec = v & 1, kind = v >> 1;
+    const void* fn = (const void*)kernels_for(dtype, vec == 1, nper).fn[kind];
     hipFuncAttributes fa;
     e = hipFuncGetAttributes(&fa, fn);
     if (e == hipSuccess && fa.localSizeBytes > 0) e = hipErrorInvalidConfiguration;
     int per_cu = 0;
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStreamThreads, 0);
-    cap[vec][dl] = cus * per_cu;
-    if (cap[vec][dl] > capmax) capmax = cap[vec][dl];
-    if (e == hipSuccess && (per_cu < 1 || (dl && (cap[vec][dl] / kGroups) * kStreamWaves < C)))
+    cap[vec][kind] = cus * per_cu;
+    if (cap[vec][kind] > capmax) capmax = cap[vec][kind];
+    if (e == hipSuccess && (per_cu < 1 || (kind == kDraft && (cap[vec][kind] / kGroups) * kStreamWaves < C)))
       e = hipErrorInvalidConfiguration;
   }
   return e;
@@ -1753,7 +2107,7 @@ hipError_t kernel_caps(int dtype, int nper, int C, int device, int (&cap)[2][2],
 // One run's launch: everything of Params but the workspace and the epoch.
 struct Plan {
   Params P;
-  Kernels K;
+  KernelFn fn;
   bool ragged, has_dl;
   int64_t wg;     // workgroups per row group
   int64_t R_t;    // 0: an empty batch, nothing to launch
@@ -1771,8 +2125,9 @@ struct Workspace {
 
 // Check one run's arguments against a configuration (C chunks per row, at
 // most max_rows target rows, resident workgroups cap) and plan its launch.
-specverify_status plan_run(const specverify_config& cfg, int C, int nper, int64_t max_rows, const int (&cap)[2][2],
-                           const specverify_inputs* in, const specverify_outputs* out, Plan& pl) {
+specverify_status plan_run(const specverify_config& cfg, int C, int nper, int64_t max_rows, const int (&cap)[2][3],
+                           const specverify_inputs* in, const specverify_outputs* out, Plan& pl,
+                           bool tree = false) {
   pl.R_t = 0;
   if (!in || !out) return SPECVERIFY_ERR_INVALID_ARGUMENT;
   const int B = in->batch;
@@ -1834,7 +2189,8 @@ specverify_status plan_run(const specverify_config& cfg, int C, int nper, int64_
   // Persistent grid: per row group, as many workgroups as the device holds,
   // never more than the busiest group has items for.
   const int64_t need = (rows_g * C + kStreamWaves - 1) / kStreamWaves;
-  int64_t wg = cap[vec ? 1 : 0][has_dl ? 1 : 0] / kGroups;
+  const int kind = tree ? kTree : has_dl ? kDraft : kNoDraft;
+  int64_t wg = cap[vec ? 1 : 0][kind] / kGroups;
   if (wg > need) wg = need;
   if (wg < 1) wg = 1;
   P.gamma = ragged ? 0 : in->gamma;
@@ -1847,7 +2203,11 @@ specverify_status plan_run(const specverify_config& cfg, int C, int nper, int64_
   P.Wg = (int32_t)wg;
   P.max_gamma = cfg.max_gamma;
   P.spin_limit = spin_of(cfg);
-  P.token_only = R_d > 0 && !has_dl;
+  P.token_only = R_d > 0 && !has_dl && !tree;
+  P.tree = tree;
+  P.parents = nullptr;
+  P.out_nodes = nullptr;
+  P.p_cand = nullptr;
   udiv_consts((uint32_t)C, P.div_c);
   udiv_consts((uint32_t)(ragged ? 1 : in->gamma + 1), P.div_g);
   P.acc_len = out->accepted_len;
@@ -1856,7 +2216,7 @@ specverify_status plan_run(const specverify_config& cfg, int C, int nper, int64_
   P.q_draft = out->q_draft;
   P.beta = out->beta;
   P.resid = out->resid_mass;
-  pl.K = kernels_for(cfg.dtype, vec, nper);
+  pl.fn = kernels_for(cfg.dtype, vec, nper).fn[kind];
   pl.ragged = ragged;
   pl.has_dl = has_dl;
   pl.wg = wg;
@@ -1883,8 +2243,7 @@ hipError_t launch_plan(Plan& pl, const Workspace& w, uint32_t epoch, hipStream_t
   P.epoch = epoch;
   if (pl.ragged)
     hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, P, w.rowinfo, w.gbounds, w.layout);
-  hipLaunchKernelGGL(pl.has_dl ? pl.K.with_draft : pl.K.no_draft, dim3((uint32_t)(pl.wg * kGroups)),
-                     dim3(kStreamThreads), 0, stream, P);
+  hipLaunchKernelGGL(pl.fn, dim3((uint32_t)(pl.wg * kGroups)), dim3(kStreamThreads), 0, stream, P);
   return hipGetLastError();
 }
 
@@ -1902,7 +2261,7 @@ struct StaticDevice {
   char* base;              // the device's copy of scratch (its device address); null until set up
   uint32_t epoch;          // the last epoch used on the device
   bool cap_known[2][3];    // [dtype][nper 1, 2, 4]
-  int cap[2][3][2][2];     // residency caps, as kernel_caps
+  int cap[2][3][2][3];     // residency caps, as kernel_caps
 };
 constexpr int kStaticDevices = 64;
 std::mutex g_static_mu;
@@ -1977,7 +2336,7 @@ struct specverify_ctx {
   int chunks;
   int nper;
   int64_t rows;            // max target rows
-  int cap[2][2];           // workgroups resident at once: [vector loads][draft logits]
+  int cap[2][3];           // workgroups resident at once: [vector loads][kind of launch]
   void* ws;
   size_t ws_bytes;
   uint64_t* xch1;
@@ -2072,6 +2431,44 @@ specverify_status specverify_run(specverify_handle h, const specverify_inputs* i
   if (ev && e == hipSuccess) e = hipEventRecord(ev[2], stream);
   if (prev != h->cfg.device) (void)hipSetDevice(prev);
   return (e == hipSuccess && e2 == hipSuccess) ? SPECVERIFY_OK : SPECVERIFY_ERR_DEVICE;
+}
+
+specverify_status specverify_run_tree(specverify_handle h, const specverify_tree_inputs* in,
+                                      const specverify_tree_outputs* out, void* hip_stream) {
+  if (!h || !in || !out) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  if (in->batch > 0 && in->cu_nodes == nullptr) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  if (in->num_nodes > 0 && in->parents == nullptr) return SPECVERIFY_ERR_INVALID_ARGUMENT;
+  // a tree batch is a ragged batch of target rows without draft logits
+  specverify_inputs li;
+  li.batch = in->batch;
+  li.gamma = 0;
+  li.cu_draft = in->cu_nodes;
+  li.num_draft_rows = in->num_nodes;
+  li.target_logits = in->target_logits;
+  li.target_stride = in->target_stride;
+  li.draft_logits = nullptr;
+  li.draft_stride = 0;
+  li.draft_tokens = in->tokens;
+  li.uniforms = in->uniforms;
+  li.temperatures = in->temperatures;
+  specverify_outputs lo;
+  lo.accepted_len = out->accepted_len;
+  lo.out_tokens = out->out_tokens;
+  lo.p_draft = lo.q_draft = lo.beta = lo.resid_mass = nullptr;
+  Plan pl;
+  const specverify_status st = plan_run(h->cfg, h->chunks, h->nper, h->rows, h->cap, &li, &lo, pl, true);
+  if (st != SPECVERIFY_OK || pl.R_t == 0) return st;
+  pl.P.parents = in->parents;
+  pl.P.out_nodes = out->out_nodes;
+  pl.P.p_cand = out->p_cand;
+  const Workspace w{h->xch1, h->dummy, h->part, h->rowinfo, h->layout, h->gbounds};
+  const uint32_t epoch = next_epoch(h->epoch);
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  if (prev != h->cfg.device && hipSetDevice(h->cfg.device) != hipSuccess) return SPECVERIFY_ERR_DEVICE;
+  const hipError_t e = launch_plan(pl, w, epoch, (hipStream_t)hip_stream);
+  if (prev != h->cfg.device) (void)hipSetDevice(prev);
+  return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_ERR_DEVICE;
 }
 
 specverify_status specverify_run_static(const specverify_config* cfg, const specverify_inputs* in,

@@ -41,6 +41,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "HEADLINE", "Inputs", "make_inputs", "token_only",
     "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "TreeWorkload", "TREE_WORKLOADS", "TreeInputs", "make_tree_inputs", "tree_shape",
 ]
 
 
@@ -243,3 +244,146 @@ def token_only(inp: Inputs) -> Inputs:
     were drawn from the draft distribution, one possible drafter's law) and
     the draft logits are dropped, so q_i = delta_{x_i}."""
     return dataclasses.replace(inp, draft=None)
+
+
+# ---------------------------------------------------------------- draft trees
+
+@dataclasses.dataclass(frozen=True)
+class TreeWorkload:
+    """A batch whose drafts form trees (EAGLE / Medusa style: the drafter's
+    Top-K candidates at every node, Perplexity "Accelerating Sonar through
+    speculation", section "EAGLE").  ``branching[d]`` children per node at
+    depth d, nodes numbered breadth-first, at most ``nodes`` per tree."""
+    name: str
+    cfg_id: int
+    batch: int
+    nodes: int
+    branching: Tuple[int, ...]
+    vocab: int
+    dtype: str
+    target: Tuple                  # as Workload.target
+    draft_sigma: float             # the drafter's scores: target row + N(0, draft_sigma^2)
+    temps: Tuple                   # ("const", T) | ("choice", (T0, T1, ...))
+
+    def replace(self, **kw) -> "TreeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+TREE_WORKLOADS = {
+    w.name: w for w in [
+        # an EAGLE-2 sized tree: 60 candidates, depth 4
+        TreeWorkload("b16_tree60_v128256_bf16", 10, 16, 60, (4, 3, 2, 2, 1, 1), 128256, "bf16",
+                     ("normal", 3.0), 1.5, ("const", 0.7)),
+        # peaked rows, so that walks go deep (parity cases)
+        TreeWorkload("b8_tree12_v32000_f32", 11, 8, 12, (3, 2, 1, 1), 32000, "f32",
+                     ("normal", 6.0), 0.5, ("choice", (0.0, 0.8, 1.0))),
+    ]
+}
+
+
+@dataclasses.dataclass
+class TreeInputs:
+    """One batch of draft trees in the packed layout of the C ABI: sequence
+    b's nodes are cu_nodes[b] .. cu_nodes[b+1] - 1 (parents as local node
+    numbers, 0 = root), its target rows and uniforms start at
+    cu_t[b] = cu_nodes[b] + b."""
+    workload: TreeWorkload
+    seed: int
+    target: np.ndarray        # [R_t, V] float32 or bf16 bits
+    parents: np.ndarray       # [N] int32
+    tokens: np.ndarray        # [N] int32
+    uniforms: np.ndarray      # [R_t] float32
+    temperatures: np.ndarray  # [B] float32
+    cu_nodes: np.ndarray      # [B+1] int32
+
+    @property
+    def batch(self) -> int:
+        return int(self.cu_nodes.shape[0] - 1)
+
+    @property
+    def cu_t(self) -> np.ndarray:
+        return (self.cu_nodes + np.arange(self.batch + 1)).astype(np.int64)
+
+    @property
+    def logit_bytes(self) -> int:
+        return int(self.target.nbytes)
+
+
+def tree_shape(nodes: int, branching: Sequence[int]) -> np.ndarray:
+    """Parents of a breadth-first tree with branching[d] children per node at
+    depth d (the last entry repeats), cut at ``nodes`` nodes."""
+    parents = []
+    level = [0]
+    d = 0
+    while len(parents) < nodes and level:
+        k = branching[min(d, len(branching) - 1)]
+        nxt = []
+        for v in level:
+            for _ in range(k):
+                if len(parents) == nodes:
+                    break
+                parents.append(v)
+                nxt.append(len(parents))
+        level = nxt
+        d += 1
+    return np.asarray(parents, dtype=np.int32)
+
+
+def make_tree_inputs(w: Union[TreeWorkload, str], seed: int = 0, *, batch: Optional[int] = None,
+                     nodes: Optional[Sequence[int]] = None) -> TreeInputs:
+    """Draw one batch of tree workload ``w``.  ``nodes`` gives each sequence's
+    node count (default: the workload's).  The candidates of node v are the
+    drafter's top-k tokens at v: the k largest scores target_v + noise
+    (distinct tokens, best first).
+
+    Streams: key (seed, cfg_id, 0): temperatures; (seed, cfg_id, 1, r):
+    target row r; (seed, cfg_id, 2, r): the drafter's noise at row r;
+    (seed, cfg_id, 3): the uniforms."""
+    if isinstance(w, str):
+        w = TREE_WORKLOADS[w]
+    if batch is not None:
+        w = w.replace(batch=batch)
+    B, V = w.batch, w.vocab
+    counts = np.full(B, w.nodes, dtype=np.int64) if nodes is None else np.asarray(nodes, dtype=np.int64)
+    meta = _stream(seed, w.cfg_id, 0)
+    if w.temps[0] == "const":
+        temps = np.full(B, w.temps[1], dtype=np.float32)
+    else:
+        choices = np.asarray(w.temps[1], dtype=np.float32)
+        temps = choices[meta.integers(0, len(choices), size=B)]
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(counts)
+    N = int(cu[-1])
+    R_t = N + B
+    store = np.float32 if w.dtype == "f32" else np.uint16
+    target = np.empty((R_t, V), dtype=store)
+    parents = np.empty(N, dtype=np.int32)
+    tokens = np.empty(N, dtype=np.int32)
+    proxy = Workload("tree-rows", w.cfg_id, B, 0, V, w.dtype, w.target, 1.0, 0.0, ("const", 1.0))
+
+    def one_sequence(b: int) -> None:
+        n = int(counts[b])
+        n0, t0 = int(cu[b]), int(cu[b]) + b
+        par = tree_shape(n, w.branching)
+        parents[n0:n0 + n] = par
+        kids = {}
+        for k, pa in enumerate(par, start=1):
+            kids.setdefault(int(pa), []).append(k)
+        for v in range(n + 1):
+            t64 = _draw_target(proxy, _stream(seed, w.cfg_id, 1, t0 + v))
+            target[t0 + v] = _round(t64, w.dtype)
+            if v in kids:
+                score = t64 + _stream(seed, w.cfg_id, 2, t0 + v).standard_normal(V) * w.draft_sigma
+                top = np.argsort(-score, kind="stable")[:len(kids[v])]
+                for k, tok in zip(kids[v], top):
+                    tokens[n0 + k - 1] = int(tok)
+
+    nthreads = min(16, os.cpu_count() or 1)
+    if B > 1 and nthreads > 1:
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(one_sequence, range(B)))
+    else:
+        for b in range(B):
+            one_sequence(b)
+    uniforms = _stream(seed, w.cfg_id, 3).random(R_t, dtype=np.float32)
+    return TreeInputs(w, seed, target, parents, tokens, uniforms, temps, cu)

@@ -78,3 +78,34 @@ def test_commit_checks():
                        ("seq_tokens", i32(2, 20)), ("seq_tokens", i32(20, 3).t()), ("appended", i32(2))):
         with pytest.raises((TypeError, ValueError)):
             check_commit_args(**dict(ok, **{field: bad}))
+
+
+def _tree_args(**over):
+    from rejection_sampling_verifier_specverify_amd.binding import check_tree_args  # noqa: F401
+    B, N = 2, 5
+    R_t = N + B
+    a = dict(vocab=V, logits_dtype=torch.float32, device=DEV, target=torch.zeros(R_t, V),
+             cu_nodes=torch.tensor([0, 3, 5], dtype=torch.int32), num_nodes=N,
+             parents=torch.zeros(N, dtype=torch.int32), tokens=torch.zeros(N, dtype=torch.int32),
+             uniforms=torch.zeros(R_t), temperatures=torch.ones(B), accepted_len=torch.zeros(B, dtype=torch.int32),
+             out_tokens=torch.zeros(R_t, dtype=torch.int32), out_nodes=torch.zeros(R_t, dtype=torch.int32),
+             p_cand=None)
+    a.update(over)
+    return a
+
+
+def test_tree_arguments():
+    from rejection_sampling_verifier_specverify_amd.binding import check_tree_args
+    assert check_tree_args(**_tree_args()) == (2, 5, 7)
+    assert check_tree_args(**_tree_args(out_nodes=None, p_cand=torch.zeros(5))) == (2, 5, 7)
+    bad = [dict(parents=torch.zeros(4, dtype=torch.int32)),          # short
+           dict(tokens=torch.zeros(5, dtype=torch.int64)),           # wrong dtype
+           dict(cu_nodes=None),                                      # missing
+           dict(target=torch.zeros(6, V)),                           # too few rows
+           dict(target=torch.zeros(7, V, dtype=torch.bfloat16)),     # wrong logits dtype
+           dict(out_nodes=torch.zeros(6, dtype=torch.int32)),        # short optional output
+           dict(p_cand=torch.zeros(5, dtype=torch.float64)),
+           dict(num_nodes=-1)]
+    for over in bad:
+        with pytest.raises((TypeError, ValueError)):
+            check_tree_args(**_tree_args(**over))
