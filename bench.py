@@ -115,12 +115,18 @@ def _pmc_rows(folder: str, counter: str):
 PROBE_COPIES = 5   # plain copies of the logits' size that --copy-probe dispatches last
 
 
-def _with_draft(name: str) -> bool:
-    """A launch of the verification kernel with draft logits (its last template argument is true)."""
+def _kernel_args(name: str):
+    """Template arguments of a verification kernel launch (dtype, vector
+    loads, chunks per lane, draft logits, tree), or None."""
     if f"{KERNEL}<" not in name:
-        return False
-    targs = name.split(f"{KERNEL}<", 1)[1].split(">", 1)[0]
-    return targs.replace(" ", "").split(",")[-1] == "true"
+        return None
+    return name.split(f"{KERNEL}<", 1)[1].split(">", 1)[0].replace(" ", "").split(",")
+
+
+def _with_draft(name: str) -> bool:
+    """A launch of the verification kernel with draft logits (not a tree launch)."""
+    a = _kernel_args(name)
+    return a is not None and a[3] == "true" and (len(a) < 5 or a[4] == "false")
 
 
 def summarize_trace(args):
@@ -236,9 +242,10 @@ def summarize_sq(args):
         with open(files[0]) as f:
             for r in csv.DictReader(f):
                 name = r["Kernel_Name"]
-                if f"{KERNEL}<" not in name:
+                a = _kernel_args(name)
+                if a is None:
                     continue
-                cls = "with_draft" if _with_draft(name) else "token_only"
+                cls = "with_draft" if _with_draft(name) else "tree" if len(a) > 4 and a[4] == "true" else "token_only"
                 rows.setdefault(r["Counter_Name"], {}).setdefault(cls, {}).setdefault(
                     int(r["Dispatch_Id"]), 0.0)
                 rows[r["Counter_Name"]][cls][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
