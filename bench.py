@@ -69,9 +69,23 @@ def trace_file(workload: str) -> str:
     return os.path.join(PROFILES, f"{KERNEL}_{workload}_kernel_trace.txt")
 
 
+def code_text(src: str) -> str:
+    """The kernel source without its // comments, trailing blanks and empty
+    lines: what the compiler sees (the source holds no "//" in strings)."""
+    out = []
+    for line in src.splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            out.append(code)
+    return "\n".join(out) + "\n"
+
+
 def source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 of the kernel source's code (comments and blank lines
+    excluded), recorded in every profile summary: a summary whose hash
+    differs was taken from other code."""
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        return hashlib.sha256(code_text(f.read()).encode()).hexdigest()
 
 
 def parse():

@@ -53,6 +53,11 @@
 // finds the sequence's first rejection n and writes accepted_len and the
 // n + 1 tokens.  The accepted length never leaves the device.
 //
+// Draft trees (specverify_run_tree, their own instantiation of the kernel)
+// stream like token-only rows; a tree's resolution loads the tree into LDS,
+// forms every candidate's p under its parent's row on four waves and walks
+// the tree on one wave (see resolve_tree).
+//
 // commit_kernel (its own call, specverify_commit) appends each sequence's
 // n + 1 emitted tokens to its token row on the device.
 //
