@@ -1590,6 +1590,78 @@ __device__ __forceinline__ float chunk_m_of(const RowSlots<NPER>& q, int cx) {
   return __uint_as_float(v);
 }
 
+// The records of a tree's rows, in the partials area of the workspace (a
+// tree launch has no phase 2): at row r, 64-bit slot 0 holds the row's
+// status and, for T = 0, its argmax; slot 1 holds p of the candidate of the
+// node whose row r is, under its parent's row.  Both carry the run's epoch.
+__device__ __forceinline__ uint64_t* tree_rec(const Params& P, int r) {
+  return (uint64_t*)(P.part + (int64_t)r * P.C * kPart);
+}
+
+// The job of one target row r of a tree, on one wave: poll the row, merge
+// its normalisers (or argmax), and form the p of each of its node's
+// children from the logit at its token with its chunk's offset and scale;
+// write the row's record and each child's record.
+template <int DT, bool VEC, int NPER>
+__device__ __forceinline__ void tree_row_job(const Params& P, int r, int lane, const uint32_t (&soff)[NPER]) {
+  using F = Fmt<DT>;
+  const int* info = (const int*)(P.rowinfo + r);
+  const int b = ld_const(info, 0);
+  const float T = __int_as_float(ld_const(info, 3));
+  const int n0 = ld_const(P.cu_draft, b);
+  const int N = ld_const(P.cu_draft, b + 1) - n0;
+  const int t0 = n0 + b;
+  const int v = r - t0;   // the node whose row this is
+  const bool sampled = t_sampled(T);
+  const float s = sampled ? kLog2e / T : 0.0f;
+  int status = 0, amax = 0;
+  float M = 0.0f, S = 0.0f;
+  RowSlots<NPER> q;
+  if (!(sampled || T == 0.0f)) {
+    status = 1;   // invalid temperature: the row was not streamed
+  } else if (!tree_poll<DT, VEC, NPER>(P, r, sampled ? 1 : 2, s, lane, soff, q)) {
+    status = 2;
+  } else if (sampled) {
+    merge_row(q, P.C, 0, s, lane, M, S);
+    if (!norm_ok(M, S)) status = 1;
+  } else {
+    float av = -__builtin_huge_valf();
+    int ak = 0x7FFFFFFF, gb = 0;
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      if (lane + 64 * j < P.C) {
+        argmax_merge(av, ak, slot_f(q.w[j][0]), (int)(uint32_t)q.w[j][1]);
+        gb |= (uint32_t)q.w[j][1] == 0xFFFFFFFFu;
+      }
+    }
+    gb = __any(gb);
+    wave_argmax(av, ak);
+    if (gb || av == -__builtin_huge_valf()) status = 1;
+    else amax = ak;
+  }
+  // the children: nodes k with parent v, 64 nodes per round
+  for (int k0 = 1; k0 <= N; k0 += 64) {
+    const int k = k0 + lane;
+    const bool in = k <= N;
+    const int pa = in ? P.parents[n0 + k - 1] : -1;
+    const int tk = in ? P.tokens[n0 + k - 1] : -1;
+    const bool child = in && pa == v;
+    float p = __builtin_nanf("");
+    if (status == 0) {   // wave-uniform
+      if (sampled) {
+        const bool ok = child && tk >= 0 && tk < P.V;
+        const float l = ok ? load_logit<DT>(P.target, r, P.tstride_b, tk) : 0.0f;
+        const float mx = chunk_m_of(q, ok ? tk / F::CH : 0);
+        p = chunk_scale(mx, M, S, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(l, s, chunk_offset(mx, s)));
+      } else {
+        p = tk == amax ? 1.0f : 0.0f;
+      }
+    }
+    if (child) slot_put(tree_rec(P, t0 + k) + 1, P.epoch, __float_as_uint(p));
+  }
+  if (lane == 0) slot_put(tree_rec(P, r), P.epoch, ((uint32_t)status << kStatusShift) | ((uint32_t)amax & kTokMask));
+}
+
 // One sequence whose N drafts form a tree (token-only candidates), on one
 // workgroup.  Perplexity "Accelerating Sonar through speculation", section
 // "EAGLE" (Top-K candidates per node), with velog "6-1편. Speculative
@@ -1653,59 +1725,50 @@ __device__ __forceinline__ void resolve_tree(const Params& P, int b, int lane, i
       tlist[toff[pa] + rank] = k;
     }
     __syncthreads();
-    // the rows
+    // the rows' records (written by the group's waves after their
+    // streaming): lane l of wave wv reads row v = wv + 4 l; a record still
+    // missing after spin_limit polls is computed here
     uint32_t soff[NPER];
     chunk_offsets(P.C, lane, kX1 * (int)sizeof(uint64_t), soff);
+    const int v = wv + kStreamWaves * lane;
+    const bool mine = v <= N;
+    const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc((void*)tree_rec(P, t0), (short)0,
+                                                      (N + 1) * P.C * kPart * (int)sizeof(float), kRsrcWord3);
+    const uint32_t off = (uint32_t)(mine ? v : 0) * (uint32_t)(P.C * kPart * (int)sizeof(float));
     int rowbad = 0;
-    for (int v = wv; v <= N; v += kStreamWaves) {
-      const int r = t0 + v;
-      const int c0 = toff[v], c1 = toff[v + 1];
-      // the logits at the first 64 candidates go out before the poll
-      const int k0 = c0 + lane < c1 ? tlist[c0 + lane] : 0;
-      float l0 = 0.0f;
-      if (sampled && c0 + lane < c1) l0 = load_logit<DT>(P.target, r, P.tstride_b, ttok[k0]);
-      RowSlots<NPER> q;
-      if (!tree_poll<DT, VEC, NPER>(P, r, sampled ? 1 : 2, s, lane, soff, q)) {
-        rowbad = max(rowbad, 2);
-        continue;
+    u32x4 w;
+    for (int k = 0;; ++k) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the loads below are read again on every turn
+      w = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kSC1);
+      const bool ready = !mine || (w[1] == P.epoch && (v == 0 || w[3] == P.epoch));
+      const uint64_t missing = __ballot(!ready);
+      if (!missing) break;
+      if (k > 2 * P.spin_limit + 16) {
+        rowbad = 2;
+        break;
       }
-      if (sampled) {
-        float M, S;
-        merge_row(q, P.C, 0, s, lane, M, S);
-        if (!norm_ok(M, S)) {
-          rowbad = max(rowbad, 1);
-          continue;
+      if (k == P.spin_limit) {
+        uint64_t m = missing;
+        while (m) {
+          const int l = __builtin_ctzll(m);
+          m &= m - 1;
+          const int vl = wv + kStreamWaves * l;
+          if ((uint32_t)__builtin_amdgcn_readlane((int)w[1], l) != P.epoch)
+            tree_row_job<DT, VEC, NPER>(P, t0 + vl, lane, soff);
+          if (vl > 0 && (uint32_t)__builtin_amdgcn_readlane((int)w[3], l) != P.epoch)
+            tree_row_job<DT, VEC, NPER>(P, t0 + tpar[vl], lane, soff);
         }
-        for (int i0 = c0; i0 < c1; i0 += 64) {
-          const int i = i0 + lane;
-          const int k = i < c1 ? tlist[i] : 0;
-          const int x = ttok[k];
-          const float l = i0 == c0 ? l0 : (i < c1 ? load_logit<DT>(P.target, r, P.tstride_b, x) : 0.0f);
-          const float mx = chunk_m_of(q, i < c1 ? x / F::CH : 0);
-          const float px =
-              chunk_scale(mx, M, S, s) * __builtin_amdgcn_exp2f(__builtin_fmaf(l, s, chunk_offset(mx, s)));
-          if (i < c1) tprob[k] = px;
-        }
+        __builtin_amdgcn_s_waitcnt(0);   // the records are in L2 before the poll below
       } else {
-        float av = -__builtin_huge_valf();
-        int ak = 0x7FFFFFFF, gb = 0;
-#pragma unroll
-        for (int j = 0; j < NPER; ++j) {
-          if (lane + 64 * j < P.C) {
-            argmax_merge(av, ak, slot_f(q.w[j][0]), (int)(uint32_t)q.w[j][1]);
-            gb |= (uint32_t)q.w[j][1] == 0xFFFFFFFFu;
-          }
-        }
-        gb = __any(gb);
-        wave_argmax(av, ak);
-        if (gb || av == -__builtin_huge_valf()) {
-          rowbad = max(rowbad, 1);
-          continue;
-        }
-        if (lane == 0) tamax[v] = ak;
-        for (int i = c0 + lane; i < c1; i += 64) tprob[tlist[i]] = ttok[tlist[i]] == ak ? 1.0f : 0.0f;
+        __builtin_amdgcn_s_sleep(2);
       }
     }
+    if (mine && rowbad == 0) {
+      rowbad = (int)(w[0] >> kStatusShift);
+      tamax[v] = (int)(w[0] & kTokMask);
+      if (v > 0) tprob[v] = __uint_as_float(w[2]);
+    }
+    rowbad = wave_max_i(rowbad);
     if (lane == 0 && rowbad) atomicMax(&tst, rowbad);
     __syncthreads();
     bad = tst;
@@ -1918,6 +1981,12 @@ __global__ __launch_bounds__(kStreamThreads, D ? 2 : 1) void verify_kernel(Param
     }
     // loads of items past the end read zero-sized buffers; let them land
     __builtin_amdgcn_s_waitcnt(0);
+  }
+  if constexpr (TREE) {
+    // the row jobs of the group's trees, spread over all its waves
+    uint32_t soff[NPER];
+    chunk_offsets(P.C, lane, kX1 * (int)sizeof(uint64_t), soff);
+    for (int p = j; p < Gr.r1 - Gr.r0; p += P.Gw) tree_row_job<DT, VEC, NPER>(P, Gr.r0 + p, lane, soff);
   }
   // Resolution: sequence k of the group goes to workgroup Wg - 1 - (k mod Wg).
   // The last workgroups of a group stream one item fewer per wave when the
