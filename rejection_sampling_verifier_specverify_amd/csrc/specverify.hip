@@ -774,16 +774,34 @@ __device__ __forceinline__ void greedy_row(const float (&x)[Fmt<DT>::L], int c, 
 // D false: the launch has no draft logits; only row 0 exists.  `x` (D
 // false, sampled rows): a drafted token; if this chunk holds it, slot 2
 // carries e_t at x instead of the absent draft's maximum.
-template <int DT, bool VEC, bool D = true>
+// Once the item is unpacked, `mid` runs (the caller's memory operations that
+// must go out before the next item's loads), then the loads of `next` go
+// into R, which the unpack freed.
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+template <typename H> struct IsNoHook { static constexpr bool value = false; };
+template <> struct IsNoHook<NoHook> { static constexpr bool value = true; };
+template <int DT, bool VEC, bool D = true, typename Hook = NoHook>
 __device__ __forceinline__ void p1_item(const Params& P, const Item& it, int lane, uint64_t* wdummy,
                                         u32x4 (&R)[2][kU], float (&E)[2][Fmt<DT>::L], float& mt,
-                                        float& md, float& st, int x = -1) {
+                                        float& md, float& st, int x = -1, const Item* next = nullptr,
+                                        Hook mid = Hook()) {
   if (!VEC) {   // element loads: issued here, not prefetched
     if (D) issue_item<DT, VEC, true>(P, it, lane, R);
     else issue_target<DT, VEC, true>(P, it, lane, R[0]);
   }
   unpack<DT>(R[0], E[0]);
   if (D) unpack<DT>(R[1], E[1]);
+  if constexpr (!IsNoHook<Hook>::value) {
+    __builtin_amdgcn_sched_barrier(0);
+    mid();
+  }
+  if (next != nullptr) {   // R is free: the next item's loads go out now
+    __builtin_amdgcn_sched_barrier(0);
+    issue_item<DT, VEC>(P, *next, lane, R);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   uint32_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
   uint64_t* dst = wdummy;
   if (it.mode() != 0) {
@@ -993,11 +1011,11 @@ __device__ __forceinline__ void help_parts(const Params& P, int r, int rd, float
 // Phase 2 of a sampled item with a draft, once its row's slots are in `q`
 // (`ready`: they all carry this run's tag).  Leaves the partials in `o` and
 // their address in `dst`; the caller stores them.
-template <int DT, bool VEC, int NPER>
+template <int DT, bool VEC, int NPER, bool HX>
 __device__ __forceinline__ void p2_item(const Params& P, const Item& it, int lane, const uint32_t (&soff)[NPER],
-                                        RowSlots<NPER>& q, bool ready,
-                                        const float (&E)[2][Fmt<DT>::L], float mt, float md, float st, float4& o,
-                                        float*& dst) {
+                                        RowSlots<NPER>& q, bool ready, const float (&Et)[Fmt<DT>::L],
+                                        const float4* sxt, const float4* sed, float mt, float md, float st,
+                                        float4& o, float*& dst) {
   const uint32_t tag = P.epoch;
   if (!ready) {
     for (int k = 0;; ++k) {
@@ -1023,7 +1041,16 @@ __device__ __forceinline__ void p2_item(const Params& P, const Item& it, int lan
   // (phase 1's st, the same values added in the same order) minus it
   float b = 0.0f;
 #pragma unroll
-  for (int k = 0; k < Fmt<DT>::L; ++k) b += min_nonneg(E[0][k], rho * E[1][k]);
+  for (int k4 = 0; k4 < Fmt<DT>::L / 4; ++k4) {
+    const float4 d = sed[k4 * 64 + lane];
+    const bool lo = HX && k4 < Fmt<DT>::L / 8;
+    const float4 t = lo ? sxt[k4 * 64 + lane]
+                        : make_float4(Et[4 * k4], Et[4 * k4 + 1], Et[4 * k4 + 2], Et[4 * k4 + 3]);
+    b += min_nonneg(t.x, rho * d.x);
+    b += min_nonneg(t.y, rho * d.y);
+    b += min_nonneg(t.z, rho * d.z);
+    b += min_nonneg(t.w, rho * d.w);
+  }
   const float bs = wave_sum(b);
   o.x = __uint_as_float(tag);
   o.y = fmaxf(st - bs, 0.0f);
@@ -1031,37 +1058,57 @@ __device__ __forceinline__ void p2_item(const Params& P, const Item& it, int lan
   dst = P.part + ((int64_t)it.r() * P.C + it.c()) * kPart;
 }
 
-// One pipeline step:
-//   phase 1 of n1 (its loads were issued two steps ago; exponentials into
-//   Efree), then the poll of cur's row, phase 2 of cur (exponentials in
-//   Ecur), then the loads of n3 into n1's buffer, now free.
-// The poll goes out after phase 1 of n1, a whole phase after cur's own
-// phase 1, so that the other chunks of its row have mostly published by
-// then.  Vector memory operations complete in order, so waiting for it also
-// waits for n2's loads, issued a step earlier: those are needed next step
-// anyway.
+// The exponentials an item keeps for its phase 2 in the wave's LDS area:
+// e_d, and with HX the lower half of e_t (the rest of e_t stays in
+// registers).  HX is taken where the chunk slots of a row need more than
+// one register set per lane (NPER > 1): there the registers would not leave
+// room for three waves per SIMD.
+template <int NPER>
+constexpr bool kHalfInLds = NPER > 1;
+template <int DT, bool HX>
+__device__ __forceinline__ void keep_item(const float (&E)[2][Fmt<DT>::L], int lane, float4* sxt, float4* sed) {
+#pragma unroll
+  for (int k4 = 0; k4 < Fmt<DT>::L / 4; ++k4) {
+    sed[k4 * 64 + lane] = make_float4(E[1][4 * k4], E[1][4 * k4 + 1], E[1][4 * k4 + 2], E[1][4 * k4 + 3]);
+    if (HX && k4 < Fmt<DT>::L / 8)
+      sxt[k4 * 64 + lane] = make_float4(E[0][4 * k4], E[0][4 * k4 + 1], E[0][4 * k4 + 2], E[0][4 * k4 + 3]);
+  }
+}
+
+// One pipeline step of a wave (launches with draft logits):
+//   phase 1 of n1, whose loads were issued a step ago; once it is unpacked,
+//   the poll of cur's row goes out, then the loads of n2 into the freed
+//   buffer; then the wait for the poll and phase 2 of cur (its e_t, or its
+//   upper half, in Ecur, the rest of its exponentials in the wave's LDS
+//   area), and n1's exponentials replace cur's there.
+// Vector memory operations complete in order: the poll, issued before n2's
+// loads, waits only for what phase 1 of n1 has consumed already.  cur's own
+// phase 1 ran a whole step earlier, so the other chunks of its row have
+// mostly published by the time the poll reads them.
+// A wave holds one item's loads and at most one and a half items'
+// exponentials in registers, which leaves room for three waves per SIMD.
 // Every path through a step issues the same memory operations (items that
 // do not exist read zero-sized buffers and write the dummy slots), so the
 // compiler's count of operations in flight is exact at every wait.
 template <int DT, bool VEC, int NPER>
 __device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy, const uint32_t (&soff)[NPER],
-                                     RowSlots<NPER>& q,
-                                     const Item& cur, const float (&Ecur)[2][Fmt<DT>::L], float cmt, float cmd,
-                                     float cst, const Item& n1, u32x4 (&R1)[2][kU], float (&Efree)[2][Fmt<DT>::L],
-                                     float& nmt, float& nmd, float& nst, const Item& n3) {
+                                     RowSlots<NPER>& q, const Item& cur, const float (&Ecur)[Fmt<DT>::L],
+                                     float4* sxt, float4* sed, float cmt, float cmd, float cst, const Item& n1,
+                                     u32x4 (&R)[2][kU], float (&Efree)[2][Fmt<DT>::L], float& nmt, float& nmd,
+                                     float& nst, const Item& n2) {
   // Phase 1 publishes what other waves' phase 2 polls for: it runs at a
   // higher issue priority than the other waves of its SIMD.
   __builtin_amdgcn_s_setprio(3);
-  p1_item<DT, VEC>(P, n1, lane, wdummy, R1, Efree, nmt, nmd, nst);
+  const bool live = cur.mode() == 1 && cur.pair();
+  p1_item<DT, VEC>(P, n1, lane, wdummy, R, Efree, nmt, nmd, nst, -1, VEC ? &n2 : nullptr,
+                   [&]() { slots_issue(P, cur.r(), live, soff, q); });
   __builtin_amdgcn_s_setprio(0);
-  slots_issue(P, cur.r(), cur.mode() == 1 && cur.pair(), soff, q);
   const bool ready = slots_ready(q, P.C, P.epoch, lane);   // consumes the poll on every path
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float* dst = (float*)(wdummy + kX1);
-  if (cur.mode() == 1 && cur.pair()) p2_item<DT, VEC, NPER>(P, cur, lane, soff, q, ready, Ecur, cmt, cmd, cst, o, dst);
+  if (live) p2_item<DT, VEC, NPER, kHalfInLds<NPER>>(P, cur, lane, soff, q, ready, Ecur, sxt, sed, cmt, cmd, cst, o, dst);
   if (lane == 0) *(float4*)dst = o;
-  __builtin_amdgcn_sched_barrier(0);
-  issue_item<DT, VEC>(P, n3, lane, R1);
+  if (n1.mode() == 1 && n1.pair()) keep_item<DT, kHalfInLds<NPER>>(Efree, lane, sxt, sed);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -1906,10 +1953,18 @@ __device__ __forceinline__ void resolve_tree(const Params& P, int b, int lane, i
 // D: the launch has draft logits (two-phase pipeline); otherwise phase 1
 // alone, with the next item's loads in flight.
 template <int DT, bool VEC, int NPER, bool D, bool TREE = false>
-__global__ __launch_bounds__(kStreamThreads, D ? 2 : 1) void verify_kernel(Params P) {
+// Three waves per SIMD with draft logits (two for the rare element loads,
+// whose larger register set would otherwise spill).
+__global__ __launch_bounds__(kStreamThreads, D ? (VEC ? 3 : 2) : 1) void verify_kernel(Params P) {
   using F = Fmt<DT>;
   __shared__ uint32_t shres[kMaxGamma + 1];
-  const int lane = threadIdx.x & 63;
+  // the exponentials each wave keeps for its current item's phase 2
+  // (launches with draft logits): e_d, and with HX the lower half of e_t
+  constexpr int kKeep4 = kHalfInLds<NPER> ? 3 * F::L / 8 : F::L / 4;   // float4 per lane
+  __shared__ float4 ssed[D ? kStreamWaves * kKeep4 * 64 : 1];
+  // the lane from mbcnt, not from threadIdx.x, which then need not live
+  // through the streaming loop
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = (int)(blockIdx.x % kGroups);
   const int wgl = (int)(blockIdx.x / kGroups);
@@ -1927,34 +1982,31 @@ __global__ __launch_bounds__(kStreamThreads, D ? 2 : 1) void verify_kernel(Param
     if (D) {
       uint32_t soff[NPER];
       chunk_offsets(P.C, lane, kX1 * (int)sizeof(uint64_t), soff);
-      u32x4 RA[2][kU], RB[2][kU];
+      u32x4 R[2][kU];
       float EA[2][F::L], EB[2][F::L];
       float amt = 0.0f, amd = 0.0f, ast = 0.0f, bmt = 0.0f, bmd = 0.0f, bst = 0.0f;
       RowSlots<NPER> q;
-      // prologue: items 0 and 1 in flight, phase 1 of item 0, item 2 in flight
+      float4* sed = ssed + wave * kKeep4 * 64;   // e_d: L / 4 float4 per lane
+      float4* sxt = sed + (F::L / 4) * 64;       // with HX, e_t's lower half: L / 8 float4 per lane
+      // prologue: item 0 loaded and through phase 1, item 1 in flight
       Item ia = make_item(P, Gr.r0, j, n_items);
       Item ib = make_item(P, Gr.r0, j + G, n_items);
-      issue_item<DT, VEC>(P, ia, lane, RA);
+      issue_item<DT, VEC>(P, ia, lane, R);
       __builtin_amdgcn_sched_barrier(0);
-      issue_item<DT, VEC>(P, ib, lane, RB);
-      __builtin_amdgcn_sched_barrier(0);
-      p1_item<DT, VEC>(P, ia, lane, wdummy, RA, EA, amt, amd, ast);
-      __builtin_amdgcn_sched_barrier(0);
-      Item ic = make_item(P, Gr.r0, j + 2 * G, n_items);
-      issue_item<DT, VEC>(P, ic, lane, RA);
+      p1_item<DT, VEC>(P, ia, lane, wdummy, R, EA, amt, amd, ast, -1, VEC ? &ib : nullptr);
+      if (ia.mode() == 1 && ia.pair()) keep_item<DT, kHalfInLds<NPER>>(EA, lane, sxt, sed);
       __builtin_amdgcn_sched_barrier(0);
       // Two steps per turn, one exit at the top: when the first step's item is
       // the wave's last, the second step runs on nothing (no waits, dummy writes).
       for (int idx = j; idx < n_items; idx += 2 * G) {
-        // cur = ia (EA), n1 = ib (RB), n2 = ic (RA, in flight)
+        // cur = ia (EA), n1 = ib (in R), n2 = ic
+        const Item ic = make_item(P, Gr.r0, idx + 2 * G, n_items);
+        step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ia, EA[0], sxt, sed, amt, amd, ast, ib, R, EB, bmt, bmd, bst, ic);
+        // cur = ib (EB), n1 = ic (in R), n2 = id
         const Item id = make_item(P, Gr.r0, idx + 3 * G, n_items);
-        step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ia, EA, amt, amd, ast, ib, RB, EB, bmt, bmd, bst, id);
-        // cur = ib (EB), n1 = ic (RA), n2 = id (RB, in flight)
-        const Item ie = make_item(P, Gr.r0, idx + 4 * G, n_items);
-        step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ib, EB, bmt, bmd, bst, ic, RA, EA, amt, amd, ast, ie);
+        step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ib, EB[0], sxt, sed, bmt, bmd, bst, ic, R, EA, amt, amd, ast, id);
         ia = ic;
         ib = id;
-        ic = ie;
       }
     } else {
       u32x4 RA[2][kU], RB[2][kU];   // row 1 is never loaded or read
