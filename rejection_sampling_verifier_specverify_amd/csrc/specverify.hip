@@ -666,8 +666,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(Params P, int4* 
 // An item in three scalar registers: target row (bits 0-23) and chunk (bits
 // 24-31); draft row (bits 0-23), mode (bits 24-25: 0 nothing to do,
 // 1 sampled, 2 greedy), whether the launch reads the position's draft
-// logits (bit 26) and whether the position has a drafted token (bit 27);
-// log2(e) / T.  Rows < 2^24 and chunks <= 256 fit.
+// logits (bit 26), whether the position has a drafted token (bit 27) and
+// whether the item exists (bit 28); log2(e) / T.  Rows < 2^24 and chunks
+// <= 256 fit.  An item's loads depend only on its rows and chunk, not on
+// the temperature, so that they can go out before T has been read.
 struct Item {
   uint32_t rc, rdf;
   float s;
@@ -677,6 +679,7 @@ struct Item {
   __device__ __forceinline__ int mode() const { return (int)((rdf >> 24) & 3u); }
   __device__ __forceinline__ bool pair() const { return (rdf >> 26) & 1u; }   // draft logits read
   __device__ __forceinline__ bool drafted() const { return (rdf >> 27) & 1u; }
+  __device__ __forceinline__ bool exists() const { return (rdf >> 28) & 1u; }
 };
 
 // Item `idx` of the row-major item list of a group whose rows start at r0.
@@ -700,7 +703,7 @@ __device__ __forceinline__ Item make_item(const Params& P, int r0, int idx, int 
   }   // any other temperature is invalid data: nothing is read
   // a token-only draft has no logits: its position streams like one without a draft
   it.rdf = (uint32_t)m.rd | (mode << 24) | ((uint32_t)(m.pair != 0 && !P.token_only) << 26) |
-           ((uint32_t)(m.pair != 0) << 27);
+           ((uint32_t)(m.pair != 0) << 27) | (1u << 28);
   return it;
 }
 
@@ -713,14 +716,14 @@ template <int DT, bool VEC, bool NOW = false>
 __device__ __forceinline__ void issue_item(const Params& P, const Item& it, int lane, u32x4 (&R)[2][kU]) {
   if (!VEC && !NOW) return;
   const int nb = P.V * Fmt<DT>::ESIZE;
-  const bool live = it.mode() != 0;
+  const bool live = it.exists();   // an invalid temperature reads what it never uses
   issue_row<DT, VEC>(chunk_rsrc(P.target, it.r(), P.tstride_b, it.c(), nb, live), lane, R[0]);
   issue_row<DT, VEC>(chunk_rsrc(P.draft, it.rd(), P.dstride_b, it.c(), nb, live && it.pair()), lane, R[1]);
 }
 template <int DT, bool VEC, bool NOW = false>
 __device__ __forceinline__ void issue_target(const Params& P, const Item& it, int lane, u32x4 (&R)[kU]) {
   if (!VEC && !NOW) return;
-  issue_row<DT, VEC>(chunk_rsrc(P.target, it.r(), P.tstride_b, it.c(), P.V * Fmt<DT>::ESIZE, it.mode() != 0),
+  issue_row<DT, VEC>(chunk_rsrc(P.target, it.r(), P.tstride_b, it.c(), P.V * Fmt<DT>::ESIZE, it.exists()),
                      lane, R);
 }
 
@@ -1539,9 +1542,10 @@ __device__ __forceinline__ void resolve_sequence(const Params& P, int b, int lan
 }
 
 // Every output -1: the batch layout (cu_draft) is invalid.
-__device__ __forceinline__ void invalid_batch(const Params& P) {
+// tid: the thread's index in its workgroup.
+__device__ __forceinline__ void invalid_batch(const Params& P, int tid) {
   const int n = P.R_t > P.B ? P.R_t : P.B;
-  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < n; t += gridDim.x * blockDim.x) {
+  for (int t = blockIdx.x * blockDim.x + tid; t < n; t += gridDim.x * blockDim.x) {
     if (t < P.B) P.acc_len[t] = -1;
     if (t < P.R_t) P.out_tokens[t] = -1;
     if (t < P.R_t && P.out_nodes) P.out_nodes[t] = -1;
@@ -1954,8 +1958,10 @@ __device__ __forceinline__ void resolve_tree(const Params& P, int b, int lane, i
 // alone, with the next item's loads in flight.
 template <int DT, bool VEC, int NPER, bool D, bool TREE = false>
 // Three waves per SIMD with draft logits (two for the rare element loads,
-// whose larger register set would otherwise spill).
-__global__ __launch_bounds__(kStreamThreads, D ? (VEC ? 3 : 2) : 1) void verify_kernel(Params P) {
+// whose larger register set would otherwise spill); at least seven for the
+// token-only and plain sampling launches with 16-byte loads and rows of at
+// most 128 chunks.
+__global__ __launch_bounds__(kStreamThreads, D ? (VEC ? 3 : 2) : (VEC && !TREE && NPER < 4 ? 7 : 1)) void verify_kernel(Params P) {
   using F = Fmt<DT>;
   __shared__ uint32_t shres[kMaxGamma + 1];
   // the exponentials each wave keeps for its current item's phase 2
@@ -1968,10 +1974,10 @@ __global__ __launch_bounds__(kStreamThreads, D ? (VEC ? 3 : 2) : 1) void verify_
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = (int)(blockIdx.x % kGroups);
   const int wgl = (int)(blockIdx.x / kGroups);
-  if (P.gbounds != nullptr && ld_const(P.layout, 0) != P.epoch * 2u) {
-    invalid_batch(P);
-    return;
-  }
+  // An invalid layout leaves every group empty, so nothing streams; the flag
+  // is acted on after the streaming loop, which keeps its read off the path
+  // to the first loads.
+  const bool bad_layout = P.gbounds != nullptr && ld_const(P.layout, 0) != P.epoch * 2u;
   const Group Gr = group_of(P, grp);
   const int n_items = (Gr.r1 - Gr.r0) * P.C;
   const int j = wgl * kStreamWaves + wave;
@@ -2033,6 +2039,10 @@ __global__ __launch_bounds__(kStreamThreads, D ? (VEC ? 3 : 2) : 1) void verify_
     }
     // loads of items past the end read zero-sized buffers; let them land
     __builtin_amdgcn_s_waitcnt(0);
+  }
+  if (bad_layout) {
+    invalid_batch(P, wave * 64 + lane);   // from the wave and lane: threadIdx.x is not kept through the loop
+    return;
   }
   if constexpr (TREE) {
     // the row jobs of the group's trees, spread over all its waves
