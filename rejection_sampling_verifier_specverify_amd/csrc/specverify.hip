@@ -571,30 +571,6 @@ __device__ __forceinline__ uint32_t udiv(uint32_t n, const uint32_t (&k)[3]) {
   return (t + ((n - t) >> k[1])) >> k[2];
 }
 
-struct RowMeta {
-  int b;      // sequence
-  int rd;     // draft row
-  int pair;   // position has a draft
-  float T;
-};
-__device__ __forceinline__ RowMeta row_meta(const Params& P, int r) {
-  RowMeta m;
-  if (P.rowinfo == nullptr) {
-    const int g1 = P.gamma + 1;
-    m.b = (int)udiv((uint32_t)r, P.div_g);
-    const int i = r - m.b * g1;
-    m.pair = i < P.gamma;
-    m.rd = m.b * P.gamma + i;
-    m.T = ld_const(P.temps, m.b);
-  } else {
-    const int* info = (const int*)(P.rowinfo + r);
-    m.b = ld_const(info, 0);
-    m.rd = ld_const(info, 1);
-    m.pair = ld_const(info, 2);
-    m.T = __int_as_float(ld_const(info, 3));
-  }
-  return m;
-}
 __device__ __forceinline__ bool t_sampled(float T) { return T >= kFltMin && T <= kFltMax; }
 __device__ __forceinline__ bool u_ok(float u) { return u >= 0.0f && u < 1.0f; }   // false for NaN
 
@@ -682,7 +658,9 @@ struct Item {
   __device__ __forceinline__ bool exists() const { return (rdf >> 28) & 1u; }
 };
 
-// Item `idx` of the row-major item list of a group whose rows start at r0.
+// Item `idx` of the row-major item list of a group whose rows start at r0:
+// its rows, chunk and flags, everything its loads need (mode and s are
+// filled in by item_mode, which reads the temperature).
 __device__ __forceinline__ Item make_item(const Params& P, int r0, int idx, int n_items) {
   Item it;
   it.rc = 0;
@@ -693,18 +671,38 @@ __device__ __forceinline__ Item make_item(const Params& P, int r0, int idx, int 
   const int c = idx - rl * P.C;
   const int r = r0 + rl;
   it.rc = (uint32_t)r | ((uint32_t)c << 24);
-  const RowMeta m = row_meta(P, r);
-  uint32_t mode = 0;
-  if (t_sampled(m.T)) {
-    mode = 1;
-    it.s = kLog2e / m.T;
-  } else if (m.T == 0.0f) {
-    mode = 2;
-  }   // any other temperature is invalid data: nothing is read
+  int rd, pair;
+  if (P.rowinfo == nullptr) {
+    const int b = (int)udiv((uint32_t)r, P.div_g);
+    const int i = r - b * (P.gamma + 1);
+    pair = i < P.gamma;
+    rd = b * P.gamma + i;
+  } else {
+    const int* info = (const int*)(P.rowinfo + r);
+    rd = ld_const(info, 1);
+    pair = ld_const(info, 2);
+  }
   // a token-only draft has no logits: its position streams like one without a draft
-  it.rdf = (uint32_t)m.rd | (mode << 24) | ((uint32_t)(m.pair != 0 && !P.token_only) << 26) |
-           ((uint32_t)(m.pair != 0) << 27) | (1u << 28);
+  it.rdf = (uint32_t)rd | ((uint32_t)(pair != 0 && !P.token_only) << 26) | ((uint32_t)(pair != 0) << 27) |
+           (1u << 28);
   return it;
+}
+// The item's mode (bits 24-25 of rdf) and s = log2(e) / T from its
+// sequence's temperature; any temperature that is neither 0 nor a usable
+// positive value is invalid data: mode 0, nothing is computed.
+__device__ __forceinline__ void item_mode(const Params& P, Item& it) {
+  if (!it.exists()) return;
+  const int r = it.r();
+  const float T = P.rowinfo == nullptr ? ld_const(P.temps, (int)udiv((uint32_t)r, P.div_g))
+                                       : __int_as_float(ld_const((const int*)(P.rowinfo + r), 3));
+  uint32_t mode = 0;
+  if (t_sampled(T)) {
+    mode = 1;
+    it.s = kLog2e / T;
+  } else if (T == 0.0f) {
+    mode = 2;
+  }
+  it.rdf |= mode << 24;
 }
 
 // The item's loads: always the same 2 kU (VEC) instructions; absent rows
@@ -1999,6 +1997,8 @@ __global__ __launch_bounds__(kStreamThreads, D ? (VEC ? 3 : 2) : (VEC && !TREE &
       Item ib = make_item(P, Gr.r0, j + G, n_items);
       issue_item<DT, VEC>(P, ia, lane, R);
       __builtin_amdgcn_sched_barrier(0);
+      item_mode(P, ia);
+      item_mode(P, ib);
       p1_item<DT, VEC>(P, ia, lane, wdummy, R, EA, amt, amd, ast, -1, VEC ? &ib : nullptr);
       if (ia.mode() == 1 && ia.pair()) keep_item<DT, kHalfInLds<NPER>>(EA, lane, sxt, sed);
       __builtin_amdgcn_sched_barrier(0);
@@ -2006,11 +2006,13 @@ __global__ __launch_bounds__(kStreamThreads, D ? (VEC ? 3 : 2) : (VEC && !TREE &
       // the wave's last, the second step runs on nothing (no waits, dummy writes).
       for (int idx = j; idx < n_items; idx += 2 * G) {
         // cur = ia (EA), n1 = ib (in R), n2 = ic
-        const Item ic = make_item(P, Gr.r0, idx + 2 * G, n_items);
+        Item ic = make_item(P, Gr.r0, idx + 2 * G, n_items);
         step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ia, EA[0], sxt, sed, amt, amd, ast, ib, R, EB, bmt, bmd, bst, ic);
+        item_mode(P, ic);
         // cur = ib (EB), n1 = ic (in R), n2 = id
-        const Item id = make_item(P, Gr.r0, idx + 3 * G, n_items);
+        Item id = make_item(P, Gr.r0, idx + 3 * G, n_items);
         step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ib, EB[0], sxt, sed, bmt, bmd, bst, ic, R, EA, amt, amd, ast, id);
+        item_mode(P, id);
         ia = ic;
         ib = id;
       }
@@ -2020,9 +2022,11 @@ __global__ __launch_bounds__(kStreamThreads, D ? (VEC ? 3 : 2) : (VEC && !TREE &
       float mt, md, st;
       Item ia = make_item(P, Gr.r0, j, n_items);
       issue_target<DT, VEC>(P, ia, lane, RA[0]);
+      item_mode(P, ia);
       for (int idx = j; idx < n_items; idx += 2 * G) {
-        const Item ib = make_item(P, Gr.r0, idx + G, n_items);
+        Item ib = make_item(P, Gr.r0, idx + G, n_items);
         issue_target<DT, VEC>(P, ib, lane, RB[0]);
+        item_mode(P, ib);
         __builtin_amdgcn_sched_barrier(0);
         int x = -1;   // a token-only draft of this row: the chunk that holds it publishes e_t at x
         if (P.token_only && ia.mode() == 1 && ia.drafted()) x = ld_const(P.tokens, ia.rd());
@@ -2030,6 +2034,7 @@ __global__ __launch_bounds__(kStreamThreads, D ? (VEC ? 3 : 2) : (VEC && !TREE &
         __builtin_amdgcn_sched_barrier(0);
         ia = make_item(P, Gr.r0, idx + 2 * G, n_items);
         issue_target<DT, VEC>(P, ia, lane, RA[0]);
+        item_mode(P, ia);
         __builtin_amdgcn_sched_barrier(0);
         x = -1;
         if (P.token_only && ib.mode() == 1 && ib.drafted()) x = ld_const(P.tokens, ib.rd());
