@@ -1972,6 +1972,16 @@ __global__ __launch_bounds__(kStreamThreads, D ? (VEC ? 3 : 2) : (VEC && !TREE &
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = (int)(blockIdx.x % kGroups);
   const int wgl = (int)(blockIdx.x / kGroups);
+  // The kernel arguments that the first logits loads depend on, requested
+  // together here: left to the branches below, their scalar loads go out one
+  // after another, a chain of round trips to a cold cache before any wave
+  // issues its first load.
+  __asm__ volatile("" ::"s"(P.gbounds), "s"(P.layout), "s"(P.rowinfo), "s"(P.target), "s"(P.draft),
+                   "s"(P.tstride_b), "s"(P.dstride_b), "s"(P.C), "s"(P.Gw), "s"(P.V), "s"(P.gamma),
+                   "s"(P.token_only), "s"(P.epoch), "s"(P.dummy), "s"(P.grow[grp]), "s"(P.grow[grp + 1]),
+                   "s"(P.gseq[grp]), "s"(P.gseq[grp + 1]));
+  __asm__ volatile("" ::"s"(P.div_c[0]), "s"(P.div_c[1]), "s"(P.div_c[2]), "s"(P.div_g[0]), "s"(P.div_g[1]),
+                   "s"(P.div_g[2]));
   // An invalid layout leaves every group empty, so nothing streams; the flag
   // is acted on after the streaming loop, which keeps its read off the path
   // to the first loads.
