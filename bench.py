@@ -415,13 +415,22 @@ def _prepare(w, seed, dev, token_only=False, inp=None):
     gamma_kw = dict(cu_draft=cu, num_draft_rows=R_d) if ragged else dict(gamma=inp.uniform_gamma)
 
     launches = [0]   # launches of this batch so far, in stream order
+    # one prepared run per copy: the arguments are checked once, and a step
+    # is the launch itself (SpecVerify.run checks them on every call)
+    prepared = [sv.prepare(t, d, small["draft_tokens"], small["uniforms"], small["temperatures"], **out, **gamma_kw)
+                for (t, d) in copies]
 
     def step(k, copy=None):
-        t, d = copies[(k if copy is None else copy) % ncopy]
+        launches[0] += 1
+        prepared[(k if copy is None else copy) % ncopy]()
+
+    def step_checked(k):
+        t, d = copies[k % ncopy]
         launches[0] += 1
         sv.run(t, d, small["draft_tokens"], small["uniforms"], small["temperatures"], **out, **gamma_kw)
 
-    return dict(inp=inp, sv=sv, out=out, step=step, launches=launches, ncopy=ncopy, copies=copies, logit_bytes=logit_bytes,
+    return dict(inp=inp, sv=sv, out=out, step=step, step_checked=step_checked, launches=launches, ncopy=ncopy,
+                copies=copies, logit_bytes=logit_bytes,
                 R_t=R_t, R_d=R_d, B=B, gamma_kw=gamma_kw, ragged=ragged)
 
 
@@ -621,6 +630,17 @@ def main():
     warm_ms = _events_time(lambda k: step(k, copy=0), 0, args.steps, stream)   # no rotation: cache-warm
     headline_launches = ctx["launches"][0]
     probe = _probe_gbps(ctx, dev, stream)
+    # host cost of one call, K enqueues timed on the host while the GPU runs
+    # behind: a prepared run (the steps above) and SpecVerify.run, which
+    # checks every tensor on every call
+    host_us = {}
+    for key, fn in (("prepared_run", step), ("run", ctx["step_checked"])):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            fn(k)
+        host_us[key] = (time.perf_counter() - t0) / args.steps * 1e6
+    torch.cuda.synchronize()
 
     # token-only drafts (draft logits NULL, q_i = delta_{x_i}) on the same batch
     tctx = _prepare(w, args.seed, dev, token_only=True, inp=token_only(inp))
@@ -700,6 +720,8 @@ def main():
         "step_frac": logit_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "warm_cache": {"ms_per_step": warm_ms, "logits_GBps": logit_bytes / (warm_ms * 1e-3) / 1e9,
                        "note": "every step reads the same copy, so part of it comes from the Infinity Cache"},
+        "launch": {"step": "a prepared run (SpecVerify.prepare: the tensors checked once per set of buffers)",
+                   "host_us_per_call": host_us},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": read_traffic(w.name), "kernel": KERNEL,
                      "alg_bytes_per_launch": logit_bytes, "kernel_us": launch_us,

@@ -179,8 +179,20 @@ def specverify_destroy(h: ctypes.c_void_p) -> None:
         raise SpecVerifyError("specverify_destroy", st)
 
 
+_DEVICES = {}
+
+
+def _cuda_device(i: int):
+    """torch.device("cuda", i), built once per ordinal."""
+    d = _DEVICES.get(i)
+    if d is None:
+        import torch
+        d = _DEVICES[i] = torch.device("cuda", i)
+    return d
+
+
 def _ptr(t) -> Optional[int]:
-    return None if t is None else int(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _check_vec(name, t, dtype, device, n, required=True):
@@ -188,6 +200,10 @@ def _check_vec(name, t, dtype, device, n, required=True):
     if t is None:
         if required and n > 0:
             raise ValueError(f"{name} is required")
+        return
+    # the common case in one expression (dtypes are singletons); the checks
+    # below only name what failed
+    if t.dtype is dtype and t.device == device and t.is_contiguous() and t.numel() >= n:
         return
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -231,6 +247,10 @@ def check_run_args(*, vocab, logits_dtype, device, target, draft, draft_tokens, 
             if name == "target" and R_t > 0:
                 raise ValueError("target logits are required")
             continue
+        sh, st = t.shape, t.stride()
+        if (t.dtype is logits_dtype and t.device == device and len(sh) == 2 and st[1] == 1 and sh[1] >= vocab
+                and st[0] >= vocab and sh[0] >= rows):
+            continue   # the common case; the checks below name what failed
         if t.dtype != logits_dtype:
             raise TypeError(f"{name} logits must be {logits_dtype}, got {t.dtype}")
         if t.device != device:
@@ -331,31 +351,21 @@ def _marshal_run(cfg, target, draft, draft_tokens, uniforms, temperatures, accep
     import torch
     want = torch.float32 if cfg.dtype == F32 else torch.bfloat16
     batch, R_d, _ = check_run_args(
-        vocab=cfg.vocab, logits_dtype=want, device=torch.device("cuda", cfg.device), target=target,
+        vocab=cfg.vocab, logits_dtype=want, device=_cuda_device(cfg.device), target=target,
         draft=draft, draft_tokens=draft_tokens, uniforms=uniforms, temperatures=temperatures,
         accepted_len=accepted_len, out_tokens=out_tokens, gamma=gamma, cu_draft=cu_draft,
         num_draft_rows=num_draft_rows,
         diagnostics=(("p_draft", p_draft), ("q_draft", q_draft), ("beta", beta), ("resid_mass", resid_mass)))
-    inp = Inputs()
-    inp.batch = batch
-    if cu_draft is None:
-        inp.gamma = int(gamma)
-        inp.cu_draft = None
-        inp.num_draft_rows = R_d
-    else:
-        inp.gamma = 0
-        inp.cu_draft = _ptr(cu_draft)
-        inp.num_draft_rows = R_d
-    inp.target_logits = _ptr(target)
-    inp.target_stride = int(target.stride(0))
     # draft None with drafted tokens: token-only drafts (q_i = delta_{x_i})
     has_draft = draft is not None and draft.numel() > 0
-    inp.draft_logits = _ptr(draft) if has_draft else None
-    inp.draft_stride = int(draft.stride(0)) if has_draft else int(cfg.vocab)
     has_tokens = draft_tokens is not None and draft_tokens.numel() > 0
-    inp.draft_tokens = _ptr(draft_tokens) if has_tokens else None
-    inp.uniforms = _ptr(uniforms)
-    inp.temperatures = _ptr(temperatures)
+    # positional construction: one call instead of a ctypes assignment per field
+    inp = Inputs(batch, 0 if cu_draft is not None else int(gamma), _ptr(cu_draft), R_d,
+                 _ptr(target), int(target.stride(0)),
+                 draft.data_ptr() if has_draft else None,
+                 int(draft.stride(0)) if has_draft else int(cfg.vocab),
+                 draft_tokens.data_ptr() if has_tokens else None,
+                 _ptr(uniforms), _ptr(temperatures))
     out = Outputs(_ptr(accepted_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),
                   _ptr(beta), _ptr(resid_mass))
     s = stream if stream is not None else torch.cuda.current_stream(cfg.device).cuda_stream
@@ -415,6 +425,21 @@ class SpecVerify:
                                    resid_mass, stream)
         specverify_run(self.handle, inp, out, s)
 
+    def prepare(self, target, draft, draft_tokens, uniforms, temperatures, accepted_len, out_tokens, *,
+                gamma: Optional[int] = None, cu_draft=None, num_draft_rows: Optional[int] = None,
+                p_draft=None, q_draft=None, beta=None, resid_mass=None) -> "PreparedRun":
+        """The same arguments as ``run``, checked once: the returned
+        ``PreparedRun`` launches on these tensors each time it is called,
+        without checking them again (a serving loop that keeps its input and
+        output buffers).  It holds references to the tensors; their storage,
+        shape and dtype must not change while it is in use."""
+        inp, out, _ = _marshal_run(self, target, draft, draft_tokens, uniforms, temperatures, accepted_len,
+                                   out_tokens, gamma, cu_draft, num_draft_rows, p_draft, q_draft, beta,
+                                   resid_mass, 0)
+        keep = (target, draft, draft_tokens, uniforms, temperatures, accepted_len, out_tokens, cu_draft, p_draft,
+                q_draft, beta, resid_mass)
+        return PreparedRun(self, inp, out, keep)
+
     def run_tree(self, target, cu_nodes, num_nodes: int, parents, tokens, uniforms, temperatures, accepted_len,
                  out_tokens, *, out_nodes=None, p_cand=None, stream=None) -> None:
         """Verification over draft trees (specverify_run_tree), on the current
@@ -463,6 +488,31 @@ class SpecVerify:
         a.next_token = _ptr(next_token)
         s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
         specverify_commit(self.handle, a, int(s))
+
+
+class PreparedRun:
+    """A run of one handle on fixed tensors (see ``SpecVerify.prepare``).
+    ``prepared()`` launches on the current torch stream of the handle's
+    device, ``prepared(stream)`` on a given HIP stream handle; like ``run``
+    it returns without synchronising."""
+
+    def __init__(self, sv: "SpecVerify", inp: Inputs, out: Outputs, keep):
+        self._sv = sv            # keeps the handle open
+        self._keep = keep        # keeps the tensors alive
+        self._inp, self._out = inp, out
+        self._fn = load_library().specverify_run
+        self._args = (ctypes.byref(inp), ctypes.byref(out))
+        self._device = sv.device
+
+    def __call__(self, stream: Optional[int] = None) -> None:
+        if not self._sv.handle:
+            raise RuntimeError("the handle of this prepared run is closed")
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream(self._device).cuda_stream
+        st = self._fn(self._sv.handle, self._args[0], self._args[1], ctypes.c_void_p(stream))
+        if st != OK:
+            raise SpecVerifyError("specverify_run", st)
 
 
 class SpecVerifyStatic:

@@ -151,3 +151,37 @@ def test_output_law_over_many_sequences(tok):
         pv = float(stats.chi2.sf(chi2, V - 1))
         print(f"[contract] law {name}: n={n} chi2={chi2:.2f} p={pv:.3g}", flush=True)
         assert pv > 1e-4, (name, counts, law)
+
+
+@pytest.mark.parametrize("name,ragged,tok", [("b64_g4_v128256_bf16", False, False),
+                                             ("b512_gragged1to7_v152064_bf16", True, False),
+                                             ("b64_g4_v128256_bf16", False, True)])
+def test_prepared_run_matches_run(name, ragged, tok):
+    """SpecVerify.prepare checks the tensors once; its launches give the same
+    bits as SpecVerify.run on the same tensors, call after call."""
+    import torch
+    inp = make_inputs(name, seed=5)
+    if tok:
+        inp = token_only(inp)
+    print(f"[contract] prepared {name} ragged={ragged} token_only={tok}", flush=True)
+    g = int(np.max(inp.gammas))
+    sv = SpecVerify(max_batch=inp.batch, max_gamma=max(g, 1), vocab=inp.workload.vocab, dtype=inp.workload.dtype)
+    dev = to_device(inp)
+    out = alloc_outputs(inp)
+    gpu_run(sv, dev, out, inp, ragged=ragged)
+    want = fetch(out)
+    kw = dict(cu_draft=dev["cu_draft"], num_draft_rows=int(inp.cu_draft[-1])) if ragged else dict(gamma=inp.uniform_gamma)
+    prepared = sv.prepare(dev["target"], dev["draft"], dev["draft_tokens"], dev["uniforms"], dev["temperatures"],
+                          **out, **kw)
+    for call in range(2):
+        for v in out.values():
+            v.fill_(-9)
+        prepared()
+        got = fetch(out)
+        for k in want:
+            assert np.array_equal(got[k], want[k], equal_nan=True), (call, k)
+    assert (want["accepted_len"] >= 0).all()
+    sv.close()
+    with pytest.raises(RuntimeError):
+        prepared()
+    torch.cuda.synchronize()
