@@ -34,8 +34,9 @@
 //             velog section 2-3 item 1; residual mass Z, item 2) go out in
 //             epoch-tagged partials.
 // The waves are software pipelined: a step runs phase 1 of item k + 1, then
-// polls item k's row and runs its phase 2, with the 16-byte loads of items
-// k + 2 and k + 3 in flight.  Logits are read with buffer loads over one
+// runs phase 2 of item k (whose row it polled as phase 1 began), with the
+// 16-byte loads of item k + 2 in flight (issued into the registers that the
+// unpack of item k + 1 has just freed).  Logits are read with buffer loads over one
 // chunk: a row without a draft gets a zero-sized buffer, so every item
 // issues the same loads and none of them touches memory it should not.
 // Without draft logits (token-only drafts, q = delta_x; or no drafts at
@@ -181,8 +182,8 @@ __device__ __forceinline__ uint32_t slot_tag(uint64_t w) { return (uint32_t)(w >
 __device__ __forceinline__ float slot_f(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
 // ------------------------------------------------------------------ wave primitives (DPP)
-// Reductions use a fixed order, so the two kernels, and every wave, reduce
-// the same data to the same bits.
+// Reductions use a fixed order, so every wave that reduces the same data (an
+// item's phase 2, a resolving wave, the help path) gets the same bits.
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
