@@ -9,7 +9,7 @@ import pytest
 from rejection_sampling_verifier_specverify_amd.binding import (
     ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, SpecVerify, SpecVerifyError)
 from rejection_sampling_verifier_specverify_amd.workloads import (
-    WORKLOADS, Workload, make_custom, make_inputs)
+    WORKLOADS, Workload, make_custom, make_inputs, token_only)
 
 from parity import alloc_outputs, compare, fetch, gpu_run, to_device
 
@@ -354,8 +354,6 @@ def test_host_validation_errors():
 
 # ---------------------------------------------------------------- token-only drafts (q = delta_x)
 
-from rejection_sampling_verifier_specverify_amd.workloads import token_only  # noqa: E402
-
 
 @pytest.mark.parametrize("name,batch", [("b64_g4_v128256_bf16", 16), ("b256_g8_v128256_bf16_mixedT", 24),
                                         ("b32_g1_v129280_bf16_mtp", 32), ("b1_g4_v32000_f32", None),
@@ -525,3 +523,33 @@ def test_final_uniform_extremes_emit_tokens_with_weight(ug, tok):
                 q /= q.sum()
             if np.maximum(p - q, 0.0).sum() > 1e-6:
                 assert p[t] - q[t] > -1e-6 * max(p[t], q[t]), (b, n, t, p[t], q[t])
+
+
+def _random_case(k):
+    """Case k of a seeded sweep over shapes: vocabularies at and around the
+    chunk edges (and V = 1), both dtypes, uniform and ragged gamma (0
+    included), flat, peaked and heavy-tailed targets, close and far drafts,
+    low, mixed and greedy temperatures, and token-only drafts."""
+    import random
+    rng = random.Random(7919 * (k + 1))
+    V = rng.choice([1, 2, 7, 64, 1000, 2047, 2048, 2049, 4097, 32000, 50257, 128256, 152064,
+                    rng.randint(1, 70000), rng.randint(70000, 200000)])
+    dtype = rng.choice(["f32", "bf16"])
+    B = rng.randint(1, 16)
+    ragged = rng.random() < 0.4
+    gamma = (rng.randint(0, 3), rng.randint(3, 8)) if ragged else rng.randint(0, 8)
+    tgt = rng.choice([("normal", rng.uniform(0.5, 8.0)), ("gumbel", rng.uniform(0.5, 4.0)),
+                      ("student_t", rng.choice([2.0, 3.0, 5.0]), rng.uniform(0.5, 3.0))])
+    temps = rng.choice([("const", rng.choice([1.0, 0.7, 0.3, 0.1, 2.0])), ("choice", (0.0, 0.05, 0.5, 1.0, 1.5))])
+    w = Workload(f"sweep{k}", 60 + k, B, gamma, V, dtype, tgt, rng.uniform(0.0, 1.2), rng.uniform(0.0, 2.0), temps)
+    inp = make_inputs(w, seed=k)
+    tok = int(inp.cu_draft[-1]) > 0 and rng.random() < 0.3
+    return (token_only(inp) if tok else inp), ragged, tok
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_random_shapes_sweep(k):
+    """A seeded sweep of odd shapes, each checked sequence by sequence against the oracle."""
+    inp, ragged, tok = _random_case(k)
+    _check(inp, ragged=True if ragged else None,
+           label=f"sweep {k} gamma={inp.workload.gamma} temps={inp.workload.temps} token_only={tok}")
