@@ -5,7 +5,10 @@ benchmarked workload (B = 64 sequences, gamma = 4 drafts, V = 128256, bf16
 logits): every target and draft row is read, p and q are formed by
 temperature softmax, the drafts are tested, the residual or bonus token is
 sampled, and accepted lengths, tokens and diagnostics are written.  A step
-is one kernel launch.
+is one kernel launch, made through a prepared run (SpecVerify.prepare: the
+tensors are checked once per set of buffers, as a serving loop that keeps
+its buffers would); the line also reports the host cost of a prepared call
+and of a call of SpecVerify.run, which checks them every time.
 
 Timing: the inputs are resident in HBM before the timed region; the steps
 rotate over enough copies of the batch (> 2x the 256 MB Infinity Cache) that
