@@ -1106,11 +1106,16 @@ __device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy
                    [&]() { slots_issue(P, cur.r(), live, soff, q); });
   __builtin_amdgcn_s_setprio(0);
   const bool ready = slots_ready(q, P.C, P.epoch, lane);   // consumes the poll on every path
+  // A row complete at the first poll marks a wave that runs behind the other
+  // waves of its row: the rest of its step runs at a raised priority, while a
+  // wave that has to wait for its row stays at the lowest.
+  if (ready) __builtin_amdgcn_s_setprio(2);
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float* dst = (float*)(wdummy + kX1);
   if (live) p2_item<DT, VEC, NPER, kHalfInLds<NPER>>(P, cur, lane, soff, q, ready, Ecur, sxt, sed, cmt, cmd, cst, o, dst);
   if (lane == 0) *(float4*)dst = o;
   if (n1.mode() == 1 && n1.pair()) keep_item<DT, kHalfInLds<NPER>>(Efree, lane, sxt, sed);
+  __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
