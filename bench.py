@@ -631,7 +631,6 @@ def main():
     ms = _events_time(step, 0, args.steps, stream)
     acc, toks = _check_outputs(ctx)          # the timed steps' last outputs are valid
     warm_ms = _events_time(lambda k: step(k, copy=0), 0, args.steps, stream)   # no rotation: cache-warm
-    headline_launches = ctx["launches"][0]
     probe = _probe_gbps(ctx, dev, stream)
     # host cost of one call, K enqueues timed on the host while the GPU runs
     # behind: a prepared run (the steps above) and SpecVerify.run, which
@@ -644,6 +643,7 @@ def main():
             fn(k)
         host_us[key] = (time.perf_counter() - t0) / args.steps * 1e6
     torch.cuda.synchronize()
+    headline_launches = ctx["launches"][0]   # every launch of the headline batch, in stream order
 
     # token-only drafts (draft logits NULL, q_i = delta_{x_i}) on the same batch
     tctx = _prepare(w, args.seed, dev, token_only=True, inp=token_only(inp))
