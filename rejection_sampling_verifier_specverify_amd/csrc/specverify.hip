@@ -1097,10 +1097,15 @@ __device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy
                                      RowSlots<NPER>& q, const Item& cur, const float (&Ecur)[Fmt<DT>::L],
                                      float4* sxt, float4* sed, float cmt, float cmd, float cst, const Item& n1,
                                      u32x4 (&R)[2][kU], float (&Efree)[2][Fmt<DT>::L], float& nmt, float& nmd,
-                                     float& nst, const Item& n2) {
+                                     float& nst, const Item& n2, bool& behind) {
   // Phase 1 publishes what other waves' phase 2 polls for: it runs at a
-  // higher issue priority than the other waves of its SIMD.
-  __builtin_amdgcn_s_setprio(3);
+  // raised issue priority, the highest for a wave that was behind the other
+  // waves of its last row (that row was complete at its first poll).
+  if (behind) {
+    __builtin_amdgcn_s_setprio(3);
+  } else {
+    __builtin_amdgcn_s_setprio(1);
+  }
   const bool live = cur.mode() == 1 && cur.pair();
   p1_item<DT, VEC>(P, n1, lane, wdummy, R, Efree, nmt, nmd, nst, -1, VEC ? &n2 : nullptr,
                    [&]() { slots_issue(P, cur.r(), live, soff, q); });
@@ -1109,6 +1114,7 @@ __device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy
   // A row complete at the first poll marks a wave that runs behind the other
   // waves of its row: the rest of its step runs at a raised priority, while a
   // wave that has to wait for its row stays at the lowest.
+  behind = ready;
   if (ready) __builtin_amdgcn_s_setprio(2);
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float* dst = (float*)(wdummy + kX1);
@@ -2020,14 +2026,17 @@ __global__ __launch_bounds__(kStreamThreads, D ? (VEC ? 3 : 2) : (VEC && !TREE &
       __builtin_amdgcn_sched_barrier(0);
       // Two steps per turn, one exit at the top: when the first step's item is
       // the wave's last, the second step runs on nothing (no waits, dummy writes).
+      bool behind = true;   // (no row yet)
       for (int idx = j; idx < n_items; idx += 2 * G) {
         // cur = ia (EA), n1 = ib (in R), n2 = ic
         Item ic = make_item(P, Gr.r0, idx + 2 * G, n_items);
-        step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ia, EA[0], sxt, sed, amt, amd, ast, ib, R, EB, bmt, bmd, bst, ic);
+        step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ia, EA[0], sxt, sed, amt, amd, ast, ib, R, EB, bmt, bmd, bst, ic,
+                            behind);
         item_mode(P, ic);
         // cur = ib (EB), n1 = ic (in R), n2 = id
         Item id = make_item(P, Gr.r0, idx + 3 * G, n_items);
-        step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ib, EB[0], sxt, sed, bmt, bmd, bst, ic, R, EA, amt, amd, ast, id);
+        step<DT, VEC, NPER>(P, lane, wdummy, soff, q, ib, EB[0], sxt, sed, bmt, bmd, bst, ic, R, EA, amt, amd, ast, id,
+                            behind);
         item_mode(P, id);
         ia = ic;
         ib = id;
