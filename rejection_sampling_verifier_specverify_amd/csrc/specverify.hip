@@ -1113,7 +1113,9 @@ __device__ __forceinline__ void step(const Params& P, int lane, uint64_t* wdummy
   const bool ready = slots_ready(q, P.C, P.epoch, lane);   // consumes the poll on every path
   // A row complete at the first poll marks a wave that runs behind the other
   // waves of its row: the rest of its step runs at a raised priority, while a
-  // wave that has to wait for its row stays at the lowest.
+  // wave that has to wait for its row stays at the lowest.  A step without a
+  // phase 2 (an item without draft logits, or none) reads an empty buffer and
+  // counts as not behind (keeping the flag across such steps measured slower).
   behind = ready;
   if (ready) __builtin_amdgcn_s_setprio(2);
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
