@@ -12,11 +12,17 @@ LIB = os.path.join(PKG, "libspecverify.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
-# -ffp-contract=off: every fused multiply-add is written out; the finisher
-# recomputes the weights of one sub-chunk and must get the owner's bits.
+# -ffp-contract=off: every fused multiply-add is written out; the resolution
+# and the help path recompute what an item's phases computed and must get
+# the same bits.
+# -amdgpu-sched-strategy=max-memory-clause: the machine scheduler keeps
+# memory operations in clauses (measured: the headline call 0.4% and the
+# single-draft batch 1.5% faster than the default strategy, results bit for
+# bit the same).
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-sched-strategy=max-memory-clause",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 
