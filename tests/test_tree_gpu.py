@@ -3,6 +3,8 @@ the C ABI, against the float64 tree oracle (tests/tree_parity.py rules).
 
 * Seeded EAGLE-like trees (f32 and bf16, sampled, greedy and mixed
   temperatures), a full-size 60-node batch at V = 128256.
+* A seeded sweep of random tree shapes (vocabulary, dtype, branching per
+  depth, node budget, temperatures).
 * Shapes: empty trees (N = 0), chains, a root with 100 children (more than
   one wave of candidates), a 255-node chain (the largest tree), duplicate
   candidates, vocabularies with a partial last chunk.
@@ -93,6 +95,31 @@ def test_seeded_trees_bf16_peaked_and_greedy():
     w = TreeWorkload("peaked", 12, 12, 40, (5, 3, 2, 1), 50000, "bf16", ("normal", 6.0), 0.5,
                      ("choice", (0.0, 0.7, 1.3)))
     _check(make_tree_inputs(w, 4), "peaked bf16 mixed T")
+
+
+def _random_tree_case(k):
+    """Case k of a seeded sweep over tree shapes: vocabularies around the
+    chunk edges, both dtypes, node budgets from 0 to 200, random branching
+    per depth (wide roots, chains), close and far drafters, sampled, greedy
+    and mixed temperatures."""
+    import random
+    rng = random.Random(104729 * (k + 1))
+    V = rng.choice([1, 2, 7, 2047, 2048, 2049, 32000, 128256, rng.randint(1, 70000), rng.randint(70000, 160000)])
+    depth = rng.randint(1, 8)
+    branching = tuple(rng.choice([1, 1, 2, 3, 4, 8, 16, 64]) for _ in range(depth))
+    w = TreeWorkload(f"tree_sweep{k}", 200 + k, rng.randint(1, 12), rng.choice([0, 1, 5, 12, 60, 200]), branching, V,
+                     rng.choice(["f32", "bf16"]),
+                     rng.choice([("normal", rng.uniform(0.5, 8.0)), ("gumbel", rng.uniform(0.5, 4.0))]),
+                     rng.uniform(0.0, 3.0),
+                     rng.choice([("const", rng.choice([1.0, 0.5, 0.1, 0.0, 2.0])), ("choice", (0.0, 0.3, 1.0, 1.5))]))
+    return make_tree_inputs(w, k)
+
+
+@pytest.mark.parametrize("k", range(60))
+def test_random_tree_shapes_sweep(k):
+    """A seeded sweep of tree shapes, each tree checked against the oracle."""
+    inp = _random_tree_case(k)
+    _check(inp, f"tree sweep {k} branching={inp.workload.branching} nodes={inp.workload.nodes}")
 
 
 def _custom(target, parents_per_seq, tokens_per_seq, u, T, dtype="f32"):
