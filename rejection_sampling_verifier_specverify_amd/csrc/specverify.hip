@@ -224,16 +224,23 @@ template <int CTRL>
 __device__ __forceinline__ int dpp_all(int v) {    // every lane has a source lane
   return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, true);
 }
+// The rows' results folded as wave_sum folds them: rows 1, 3 take lane 15,
+// 47, then rows 2, 3 lane 31, so lane 63 holds the result; rows a step does
+// not write get `fill`, the operation's identity.
+constexpr int kKeyMin = -0x7FFFFFFF - 1;
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_rows_i(int v, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, CTRL, ROW_MASK, 0xf, false);
+}
 __device__ __forceinline__ float wave_max(float f) {
   int v = f2key(f);
   v = max(v, dpp_all<0xB1>(v));
   v = max(v, dpp_all<0x4E>(v));
   v = max(v, dpp_all<0x141>(v));
   v = max(v, dpp_all<0x140>(v));
-  // every lane holds its row's max: fold the four rows on the scalar unit
-  const int a = max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16));
-  const int b = max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48));
-  return key2f(max(a, b));
+  v = max(v, dpp_rows_i<0x142, 0xa>(v, kKeyMin));
+  v = max(v, dpp_rows_i<0x143, 0xc>(v, kKeyMin));
+  return key2f(__builtin_amdgcn_readlane(v, 63));
 }
 // Inclusive prefix sum over the 64 lanes, fixed association.
 __device__ __forceinline__ float wave_scan(float v, int lane) {
@@ -256,16 +263,18 @@ __device__ __forceinline__ int wave_min_i(int v) {
   v = min(v, dppi<0x4E>(v));
   v = min(v, dppi<0x141>(v));
   v = min(v, dppi<0x140>(v));
-  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  v = min(v, dpp_rows_i<0x142, 0xa>(v, 0x7FFFFFFF));
+  v = min(v, dpp_rows_i<0x143, 0xc>(v, 0x7FFFFFFF));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 __device__ __forceinline__ int wave_max_i(int v) {
   v = max(v, dppi<0xB1>(v));
   v = max(v, dppi<0x4E>(v));
   v = max(v, dppi<0x141>(v));
   v = max(v, dppi<0x140>(v));
-  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  v = max(v, dpp_rows_i<0x142, 0xa>(v, kKeyMin));
+  v = max(v, dpp_rows_i<0x143, 0xc>(v, kKeyMin));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 // (value, index): larger value wins, lower index on ties.
 // (v2, k2) wins over (v, k) if larger, or equal with a lower index.  Written
